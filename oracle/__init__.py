@@ -1,0 +1,13 @@
+"""CPU oracle for the ConvLinear4bit hot path -- test infrastructure only.
+
+Importable from tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg;
+never from the product package.
+"""
+from .convrot_oracle import *  # noqa: F401,F403
+from .convrot_oracle import (  # noqa: F401
+    INT4_QMAX, INT4_QMIN, base_regular_hadamard, bf16_bits_to_f32, check_group_size,
+    convlinear4bit, dequantize, f32_to_bf16_bits, int_gemm, is_power_of_four, log4,
+    pack_int4, padded_k, quantize, quantize_weight, reference_linear_fp64,
+    regular_hadamard, rotate_groups, rotate_quantize, row_scales, to_f32, unpack_int4,
+    w4a4_linear_from_codes, zero_pad_columns,
+)

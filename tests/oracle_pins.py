@@ -1,0 +1,414 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes the oracle module and raises AssertionError when
+the oracle disagrees with a closed form, an invariant, brute force on tiny
+inputs, a library routine, or a value printed on the pages.  The same functions
+are run against deliberately broken copies of the oracle in
+``test_oracle_mutations.py`` to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import functools
+import math
+import pathlib
+
+import numpy as np
+
+GOLDEN = pathlib.Path(__file__).parent / "golden"
+SIZES = (4, 16, 64, 256, 1024)
+
+
+# ---------------------------------------------------------------- helpers
+def _closed_form_entry(i: int, j: int, g: int) -> int:
+    """(-1)^(number of base-4 digits where i and j agree), by digit loops."""
+    equal = 0
+    n = g
+    while n > 1:
+        if i % 4 == j % 4:
+            equal += 1
+        i //= 4
+        j //= 4
+        n //= 4
+    return -1 if equal % 2 else 1
+
+
+def _sylvester(n: int) -> np.ndarray:
+    h = np.ones((1, 1))
+    h2 = np.array([[1.0, 1.0], [1.0, -1.0]])
+    while h.shape[0] < n:
+        h = np.kron(h, h2)
+    return h
+
+
+@functools.lru_cache(maxsize=1)
+def _order4_hadamards():
+    """All order-4 +-1 matrices M with M M^T = 4 I, by exhaustive enumeration of 2^16."""
+    bits = np.arange(1 << 16, dtype=np.int64)[:, None] >> np.arange(16)[None, :]
+    mats = np.where(bits & 1, 1.0, -1.0).reshape(-1, 4, 4)
+    gram = np.einsum("aij,akj->aik", mats, mats)
+    keep = np.all(gram == 4 * np.eye(4), axis=(1, 2))
+    return tuple(mats[keep])
+
+
+def _is_regular(h: np.ndarray) -> bool:
+    rs = h.sum(axis=1)
+    cs = h.sum(axis=0)
+    return bool(np.all(rs == rs[0]) and np.all(cs == rs[0]))
+
+
+def _bf16_values(rng, shape, scale=1.0):
+    import torch
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+# ---------------------------------------------------------------- group size
+def pin_power_of_four_golden(o):
+    """Golden cases: the author's sizes and the 2^58 case of the review."""
+    for line in (GOLDEN / "power_of_four.txt").read_text().splitlines():
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        verdict, expr = line.split(None, 1)
+        value = eval(expr, {"__builtins__": {}})  # integer literals / powers only
+        assert o.is_power_of_four(value) == (verdict == "accept"), (verdict, expr)
+        if verdict == "reject":
+            try:
+                o.check_group_size(value)
+            except ValueError as e:
+                assert str(e) == f"Regular Hadamard size must be a power of 4, got {value}"
+            else:
+                raise AssertionError(f"{expr} accepted")
+    # The float test the review replaces really does reject 4^29.
+    assert math.log(2 ** 58, 4) % 1 != 0
+    assert o.is_power_of_four(2 ** 58)
+
+
+# ---------------------------------------------------------------- Hadamard
+def pin_hadamard_definition(o):
+    """Def. 2.1: entries +-1 and H H^T = g I."""
+    for g in SIZES:
+        h = o.regular_hadamard(g)
+        assert h.shape == (g, g)
+        assert np.all(np.abs(h) == 1.0)
+        assert np.array_equal(h @ h.T, g * np.eye(g))
+
+
+def pin_regular(o):
+    """Def. 2.3 (reading): every row and column sums to the same value, +sqrt(g)."""
+    for g in SIZES:
+        h = o.regular_hadamard(g)
+        r = math.isqrt(g)
+        assert np.all(h.sum(axis=0) == r) and np.all(h.sum(axis=1) == r)
+
+
+def pin_closed_form_entries(o):
+    """Thm. 2.3 (Kronecker construction): entry formula over base-4 digits."""
+    for g in (4, 16, 64, 256):
+        h = o.regular_hadamard(g)
+        ref = np.array([[_closed_form_entry(i, j, g) for j in range(g)] for i in range(g)])
+        assert np.array_equal(h, ref)
+    h = o.regular_hadamard(1024)
+    rng = np.random.default_rng(7)
+    for i, j in rng.integers(0, 1024, size=(4000, 2)):
+        assert h[i, j] == _closed_form_entry(int(i), int(j), 1024)
+
+
+def pin_symmetric_involution(o):
+    for g in SIZES:
+        h = o.regular_hadamard(g)
+        assert np.array_equal(h, h.T)
+        assert np.array_equal(h @ h, g * np.eye(g))
+
+
+def pin_column_sum_squared(o):
+    """Thm. 2.1 (reading): sum_j (column sum_j)^2 = g^2 for every H-matrix."""
+    rng = np.random.default_rng(3)
+    for g in SIZES:
+        mats = [o.regular_hadamard(g), _sylvester(g)]
+        for _ in range(3):
+            p = np.eye(g)[rng.permutation(g)]
+            d = np.diag(rng.choice([-1.0, 1.0], size=g))
+            mats.append(d @ p @ _sylvester(g))
+        for h in mats:
+            assert np.sum(h.sum(axis=0) ** 2) == g * g
+
+
+def pin_order4_enumeration(o):
+    """Brute force over all 2^16 order-4 +-1 matrices.
+
+    768 are Hadamard.  Every one has column discrepancy max_j |column sum| >= 2
+    = sqrt(4) (Thm. 2.1 with Def. 2.2, reading); the 48 regular ones (Def. 2.3)
+    attain that minimum, and the base matrix is one of them.
+    """
+    had = _order4_hadamards()
+    assert len(had) == 768
+    disc = [np.max(np.abs(h.sum(axis=0))) for h in had]
+    assert min(disc) == 2
+    regular = [h for h in had if _is_regular(h)]
+    assert len(regular) == 48
+    assert all(np.max(np.abs(h.sum(axis=0))) == 2 for h in regular)
+    base = o.base_regular_hadamard()
+    assert any(np.array_equal(base, h) for h in regular)
+    assert np.all(base.sum(axis=0) == 2)
+
+
+def pin_kronecker_closure(o):
+    """Thm. 2.3: Kronecker products of regular H-matrices are regular H-matrices."""
+    regular = [h for h in _order4_hadamards() if _is_regular(h)]
+    for a in regular:
+        for b in regular:
+            k = np.kron(a, b)
+            assert np.array_equal(k @ k.T, 16 * np.eye(16))
+            assert _is_regular(k)
+    for g in SIZES[1:]:
+        assert _is_regular(o.regular_hadamard(g))
+
+
+def pin_sylvester_not_regular(o):
+    s = _sylvester(256)
+    cs = s.sum(axis=0)
+    assert sorted(set(cs.tolist())) == [0.0, 256.0]
+    assert not _is_regular(s)
+    assert _is_regular(o.regular_hadamard(256))
+
+
+# ---------------------------------------------------------------- rotation
+def pin_rotation_constant_row(o):
+    """A constant row rotates to the same constant (equal column sums; Fig. 1)."""
+    for g in SIZES:
+        for c in (3.0, -0.75, 3.0 * 2.0 ** -20):
+            x = np.full((2, 2 * g), c)
+            y = o.rotate_groups(x, g)
+            assert np.array_equal(y, x)
+
+
+def pin_rotation_vs_sylvester_energy(o):
+    """Fig. 1/2 direction: Sylvester concentrates a row-wise outlier, regular does not."""
+    g, c = 256, 3.0
+    x = np.full((1, g), c)
+    syl = (x @ _sylvester(g).T) / 16.0
+    assert np.max(np.abs(syl)) == 48.0
+    assert np.max(np.abs(o.rotate_groups(x, g))) == 3.0
+
+
+def pin_rotation_one_hot(o):
+    for g in SIZES:
+        h = o.regular_hadamard(g)
+        for j in (0, 1, g // 3, g - 1):
+            x = np.zeros((1, g))
+            x[0, j] = 1.0
+            y = o.rotate_groups(x, g)
+            assert np.array_equal(y[0], h[j] / math.isqrt(g))
+            ref = np.array([_closed_form_entry(i, j, g) for i in range(g)]) / math.isqrt(g)
+            assert np.array_equal(y[0], ref)
+
+
+def pin_rotation_involution(o):
+    """(H/sqrt g)^2 = I: rotating twice returns small-integer inputs exactly."""
+    rng = np.random.default_rng(5)
+    for g in SIZES:
+        x = rng.integers(-20, 21, size=(3, 3 * g)).astype(np.float64)
+        assert np.array_equal(o.rotate_groups(o.rotate_groups(x, g), g), x)
+
+
+def pin_rotation_norm_linearity(o):
+    rng = np.random.default_rng(6)
+    for g in SIZES:
+        x = rng.standard_normal((4, 2 * g))
+        z = rng.standard_normal((4, 2 * g))
+        yx = o.rotate_groups(x, g)
+        for w in range(2):
+            a = np.linalg.norm(x[:, w * g:(w + 1) * g], axis=1)
+            b = np.linalg.norm(yx[:, w * g:(w + 1) * g], axis=1)
+            assert np.allclose(a, b, rtol=1e-13)
+        assert np.allclose(o.rotate_groups(2 * x - z, g), 2 * yx - o.rotate_groups(z, g),
+                           rtol=1e-12, atol=1e-12)
+
+
+def pin_rotation_brute_force_padded(o):
+    """Pure-Python loops on tiny ragged rows, zero padding to whole windows."""
+    rng = np.random.default_rng(8)
+    for g, K in ((4, 7), (16, 37), (64, 65), (16, 16)):
+        x = rng.integers(-9, 10, size=(3, K)).astype(np.float64) / 4.0
+        y = o.rotate_groups(x, g)
+        Kp = -(-K // g) * g
+        assert y.shape == (3, Kp)
+        k = int(round(math.log(g, 4)))
+        for m in range(3):
+            for p in range(Kp):
+                w0 = (p // g) * g
+                acc = 0.0
+                for j in range(g):
+                    xv = x[m, w0 + j] if w0 + j < K else 0.0
+                    acc += _closed_form_entry(p - w0, j, g) * xv
+                assert y[m, p] == acc / 2 ** k
+
+
+def pin_rotation_exact_fsum(o):
+    """The float64 rotation equals the exactly rounded sum (math.fsum) on bf16 data."""
+    rng = np.random.default_rng(9)
+    for g in (16, 256, 1024):
+        x = _bf16_values(rng, (3, 2 * g), scale=1.0)
+        x[0, :] *= 50.0
+        x[:, 5] *= 30.0
+        y = o.rotate_groups(x, g)
+        k = int(round(math.log(g, 4)))
+        for _ in range(40):
+            m = int(rng.integers(0, 3))
+            p = int(rng.integers(0, 2 * g))
+            w0 = (p // g) * g
+            terms = [_closed_form_entry(p - w0, j, g) * float(x[m, w0 + j]) for j in range(g)]
+            assert y[m, p] == math.fsum(terms) / 2 ** k
+
+
+# ---------------------------------------------------------------- quantization
+def pin_quant_round_trip(o):
+    """Rows s * (integers in [-7, 7]) with 7 present come back exactly."""
+    rng = np.random.default_rng(10)
+    ints = rng.integers(-7, 8, size=(6, 64))
+    ints[:, 3] = 7
+    ints[2, 3] = -7
+    ints[2, 9] = 5
+    s = (rng.integers(1, 64, size=6) * np.exp2(rng.integers(-10, 4, size=6))).astype(np.float32)
+    yf = (ints * s[:, None].astype(np.float64)).astype(np.float32)
+    sc = o.row_scales(yf)
+    assert np.array_equal(sc, s)
+    assert np.array_equal(o.quantize(yf, sc), ints.astype(np.int8))
+
+
+def pin_quant_absmax_and_range(o):
+    rng = np.random.default_rng(11)
+    yf = (rng.standard_normal((50, 300)) * np.exp2(rng.integers(-8, 8, size=(50, 1)))).astype(np.float32)
+    s = o.row_scales(yf)
+    q = o.quantize(yf, s)
+    am = np.argmax(np.abs(yf), axis=1)
+    assert np.array_equal(np.abs(q[np.arange(50), am]), np.full(50, 7))
+    assert q.min() >= -7 and q.max() <= 7
+
+
+def pin_quant_power_of_two_scaling(o):
+    rng = np.random.default_rng(12)
+    yf = rng.standard_normal((8, 128)).astype(np.float32)
+    s = o.row_scales(yf)
+    q = o.quantize(yf, s)
+    for e in (-5, 3):
+        y2 = (yf * np.float32(2.0 ** e)).astype(np.float32)
+        s2 = o.row_scales(y2)
+        assert np.array_equal(s2, (s * np.float32(2.0 ** e)).astype(np.float32))
+        assert np.array_equal(o.quantize(y2, s2), q)
+
+
+def pin_quant_zero_row(o):
+    yf = np.zeros((2, 32), dtype=np.float32)
+    yf[1, 4] = 1.0
+    s = o.row_scales(yf)
+    assert s[0] == 0.0
+    q = o.quantize(yf, s)
+    assert np.all(q[0] == 0)
+    assert q[1, 4] == 7
+
+
+def pin_quant_ties_even(o):
+    """Round half to even: 2.5 -> 2, 3.5 -> 4, -2.5 -> -2, 0.5 -> 0, 1.5 -> 2."""
+    yf = np.array([[7.0, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, -6.5]], dtype=np.float32)
+    s = o.row_scales(yf)
+    assert s[0] == np.float32(1.0)
+    assert o.quantize(yf, s).tolist() == [[7, 2, 4, -2, 0, 0, 2, -6]]
+
+
+def pin_pack_layout(o):
+    assert o.pack_int4(np.array([[1, -1]])).tolist() == [[0xF1]]
+    assert o.pack_int4(np.array([[-8, 7]])).tolist() == [[0x78]]
+    assert o.pack_int4(np.array([[0, -8, 3, 2]])).tolist() == [[0x80, 0x23]]
+    allb = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    assert np.array_equal(o.pack_int4(o.unpack_int4(allb)), allb)
+    codes = np.array([[c0, c1] for c0 in range(-8, 8) for c1 in range(-8, 8)]).reshape(1, -1)
+    assert np.array_equal(o.unpack_int4(o.pack_int4(codes)), codes.astype(np.int8))
+    # brute-force nibble reading: element 2j low nibble, 2j+1 high nibble
+    b = o.pack_int4(codes)
+    for j in range(b.shape[1]):
+        lo, hi = int(b[0, j]) & 15, int(b[0, j]) >> 4
+        assert (lo - 16 if lo >= 8 else lo) == codes[0, 2 * j]
+        assert (hi - 16 if hi >= 8 else hi) == codes[0, 2 * j + 1]
+
+
+# ---------------------------------------------------------------- GEMM, dequant
+def pin_int_gemm_brute_force(o):
+    rng = np.random.default_rng(13)
+    for M, N, K in ((3, 5, 64), (7, 2, 16), (16, 16, 64)):
+        qx = rng.integers(-8, 8, size=(M, K))
+        qw = rng.integers(-8, 8, size=(N, K))
+        acc = o.int_gemm(qx.astype(np.int8), qw.astype(np.int8))
+        for m in range(M):
+            for n in range(N):
+                s = 0
+                for k in range(K):
+                    s += int(qx[m, k]) * int(qw[n, k])
+                assert acc[m, n] == s
+    K = 16384
+    full = np.full((1, K), -8, dtype=np.int8)
+    assert o.int_gemm(full, full)[0, 0] == 64 * K
+
+
+def pin_bf16_rounding_vs_torch(o):
+    import torch
+    rng = np.random.default_rng(14)
+    z = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, size=20000))).astype(np.float32)
+    u = z.view(np.uint32).copy()
+    u[:2000] = (u[:2000] & 0xFFFF0000) | 0x8000       # exact ties
+    u[2000:4000] = (u[2000:4000] & 0xFFFF0000) | 0x7FFF
+    u[4000:6000] = (u[4000:6000] & 0xFFFF0000) | 0x8001
+    z = u.view(np.float32)
+    ref = torch.from_numpy(z.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(o.f32_to_bf16_bits(z), ref)
+    assert np.array_equal(o.bf16_bits_to_f32(ref),
+                          torch.from_numpy(ref.view(np.int16).copy()).view(torch.bfloat16)
+                          .to(torch.float32).numpy())
+
+
+def pin_end_to_end_closed_form(o):
+    """Constant rows: codes +-7, scales |c|/7, acc = 49 K' sign, out = bf16(K' c d + b)."""
+    import torch
+    for g, K, c, d, b in ((16, 64, 7.0, 14.0, 0.5), (16, 64, 0.875, 0.4375, 3.0),
+                          (256, 512, -3.5, 1.75, None),
+                          (64, 100, 0.875, -7.0, -2.0), (1024, 1024, 2.0, 3.5, None)):
+        Kp = -(-K // g) * g
+        x = np.full((3, K), c)
+        w = np.full((2, K), d)
+        bias = None if b is None else np.full(2, b, dtype=np.float32)
+        r = o.convlinear4bit(x, w, bias, g)
+        padded = Kp != K
+        if not padded:
+            assert np.all(np.abs(r["x"]["codes"]) == 7) and np.all(np.abs(r["w"]["codes"]) == 7)
+            assert np.all(r["x"]["scale"] == np.float32(abs(c) / 7))
+            assert np.all(r["w"]["scale"] == np.float32(abs(d) / 7))
+            assert np.all(r["acc"] == 49 * Kp * int(np.sign(c) * np.sign(d)))
+        exact = K * c * d + (0.0 if b is None else b)
+        want = torch.tensor([exact], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+        if not padded:
+            assert np.all(r["out_bits"] == np.uint16(want.numpy().view(np.uint16)[0]))
+        else:
+            out = o.bf16_bits_to_f32(r["out_bits"])
+            assert np.allclose(out, exact, rtol=0.15)
+
+
+def pin_int4_linear_semantics(o):
+    """[KITCHEN] int4_linear: x @ w^T on unpacked codes, row scale, column scale, bias."""
+    rng = np.random.default_rng(15)
+    qx = rng.integers(-8, 8, size=(5, 32)).astype(np.int8)
+    qw = rng.integers(-8, 8, size=(4, 32)).astype(np.int8)
+    sx = np.array([0.5, 0.25, 2.0, 1.0, 0.125], dtype=np.float32)
+    sw = np.array([1.0, 0.5, 4.0, 0.0625], dtype=np.float32)
+    b = np.array([1.0, -2.0, 0.0, 0.5], dtype=np.float32)
+    r = o.w4a4_linear_from_codes(qx, sx, qw, sw, b)
+    acc = qx.astype(np.int64) @ qw.astype(np.int64).T
+    exact = acc * sx[:, None].astype(np.float64) * sw[None, :].astype(np.float64) + b[None, :]
+    # power-of-two scales keep every product exact; bf16 of exact values
+    import torch
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(r["out_bits"], want.view(np.uint16))
+    assert np.array_equal(r["acc"], acc)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,136 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that the pins catch them.
+
+Each mutation replaces one oracle function through monkeypatch for the duration
+of one test; the designated pins must then fail.  This shows the pins are
+sharp enough to catch a dropped term, a wrong sign, index or operand order.
+"""
+import numpy as np
+import pytest
+
+from oracle import convrot_oracle as O
+from tests import oracle_pins as P
+
+_orig = {name: getattr(O, name) for name in dir(O) if not name.startswith("__")}
+
+
+def _sylvester_base():
+    h2 = np.array([[1.0, 1.0], [1.0, -1.0]])
+    return np.kron(h2, h2)
+
+
+def _one_entry_flipped():
+    h = _orig["base_regular_hadamard"]().copy()
+    h[0, 1] = -h[0, 1]
+    return h
+
+
+def _rotate_unnormalised(a, g):
+    return _orig["rotate_groups"](a, g) * 2.0 ** _orig["log4"](g)
+
+
+def _rotate_strided_windows(a, g):
+    h = _orig["regular_hadamard"](g)
+    ap = _orig["zero_pad_columns"](a, g)
+    rows, kp = ap.shape
+    win = ap.reshape(rows, g, kp // g).transpose(0, 2, 1)     # wrong: strided windows
+    y = (win @ h.T * 2.0 ** -_orig["log4"](g)).transpose(0, 2, 1)
+    return y.reshape(rows, kp)
+
+
+def _padded_k_floor(K, g):
+    return max(g, (int(K) // g) * g)
+
+
+def _zero_pad_floor(a, g):
+    a = np.asarray(a, dtype=np.float64)
+    kp = _padded_k_floor(a.shape[1], g)
+    out = np.zeros((a.shape[0], kp))
+    n = min(kp, a.shape[1])
+    out[:, :n] = a[:, :n]
+    return out
+
+
+def _row_scales_q8(yf, qmax=7):
+    return _orig["row_scales"](yf, 8)
+
+
+def _quantize_half_up(yf, scale, qmax=7, qmin=-8):
+    yf = np.asarray(yf, dtype=np.float32)
+    q = np.zeros(yf.shape, dtype=np.int8)
+    live = scale > 0
+    z = (yf[live] / scale[live, None]).astype(np.float32)
+    q[live] = np.clip(np.floor(z + np.float32(0.5)), qmin, qmax).astype(np.int8)
+    return q
+
+
+def _pack_swapped(q):
+    q = np.asarray(q, dtype=np.int64)
+    return ((q[:, 1::2] & 0xF) | ((q[:, 0::2] & 0xF) << 4)).astype(np.uint8)
+
+
+def _unpack_unsigned(b):
+    b = np.asarray(b, dtype=np.int64)
+    out = np.empty((b.shape[0], 2 * b.shape[1]), dtype=np.int8)
+    out[:, 0::2] = b & 0xF
+    out[:, 1::2] = (b >> 4) & 0xF
+    return out
+
+
+def _gemm_bf16_accumulate(qx, qw):
+    import torch
+    a = torch.from_numpy(np.asarray(qx, dtype=np.float32)).to(torch.bfloat16)
+    b = torch.from_numpy(np.asarray(qw, dtype=np.float32)).to(torch.bfloat16)
+    out = torch.zeros((a.shape[0], b.shape[0]), dtype=torch.bfloat16)
+    for k in range(a.shape[1]):  # bf16 running sum, as in the reviewed eager code
+        out = (out + a[:, k:k + 1] * b[:, k][None, :]).to(torch.bfloat16)
+    return out.to(torch.float64).numpy().astype(np.int64)
+
+
+def _dequant_bias_first(acc, sx, sw, bias=None):
+    z = np.asarray(acc, dtype=np.float32)
+    if bias is not None:
+        z = (z + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    z = (z * np.asarray(sx, dtype=np.float32)[:, None]).astype(np.float32)
+    z = (z * np.asarray(sw, dtype=np.float32)[None, :]).astype(np.float32)
+    return _orig["f32_to_bf16_bits"](z)
+
+
+def _dequant_no_wscale(acc, sx, sw, bias=None):
+    return _orig["dequantize"](acc, sx, np.ones_like(np.asarray(sw, dtype=np.float32)), bias)
+
+
+def _bf16_truncate(z):
+    u = np.asarray(z, dtype=np.float32).view(np.uint32)
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+MUTATIONS = {
+    "sylvester_base": ({"base_regular_hadamard": _sylvester_base}, ["pin_regular"]),
+    "negated_base": ({"base_regular_hadamard": lambda: -_orig["base_regular_hadamard"]()},
+                     ["pin_regular"]),
+    "sign_flip_entry": ({"base_regular_hadamard": _one_entry_flipped},
+                        ["pin_hadamard_definition"]),
+    "unnormalised": ({"rotate_groups": _rotate_unnormalised}, ["pin_rotation_constant_row"]),
+    "strided_windows": ({"rotate_groups": _rotate_strided_windows},
+                        ["pin_rotation_brute_force_padded"]),
+    "floor_padding": ({"zero_pad_columns": _zero_pad_floor, "padded_k": _padded_k_floor},
+                      ["pin_rotation_brute_force_padded"]),
+    "qmax_8": ({"row_scales": _row_scales_q8}, ["pin_quant_round_trip"]),
+    "round_half_up": ({"quantize": _quantize_half_up}, ["pin_quant_ties_even"]),
+    "swapped_nibbles": ({"pack_int4": _pack_swapped}, ["pin_pack_layout"]),
+    "unsigned_unpack": ({"unpack_int4": _unpack_unsigned}, ["pin_pack_layout"]),
+    "bf16_accumulation": ({"int_gemm": _gemm_bf16_accumulate}, ["pin_int_gemm_brute_force"]),
+    "bias_before_scale": ({"dequantize": _dequant_bias_first}, ["pin_end_to_end_closed_form", "pin_int4_linear_semantics"]),
+    "dropped_weight_scale": ({"dequantize": _dequant_no_wscale}, ["pin_int4_linear_semantics"]),
+    "bf16_truncation": ({"f32_to_bf16_bits": _bf16_truncate}, ["pin_bf16_rounding_vs_torch"]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    patches, pins = MUTATIONS[name]
+    for attr, fn in patches.items():
+        monkeypatch.setattr(O, attr, fn)
+    for pin_name in pins:
+        with pytest.raises((AssertionError, ValueError)):
+            getattr(P, pin_name)(O)
