@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the ConvLinear4bit forward pass on one MI355X.
+
+One step = the whole hot path on one batch: rotate + quantize the activations
+(convrot_rotate_quant_act) and the W4A4 GEMM with the fused dequant epilogue
+(convrot_w4a4_gemm), i.e. the two kernels convrot_w4a4_linear enqueues, launched through
+the C ABI.  The weights are rotated and quantized once, before timing (offline path).
+
+Prints ONE JSON line.  `value` is the full-layer throughput 2 M N K' / step time.  The
+`roofline` object is for the dominant kernel (the GEMM, int8 matrix cores); the
+rotate+quantize kernel's HBM roofline is reported alongside.  Per-kernel durations come
+from HIP events recorded on the launch stream inside the timed region.  The CPU oracle is
+timed on a bounded sample of the same workload (`cpu_baseline`).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 linear TOPS + rotate-quant GB/s (% of roofline) at M=4608,K=3072,g=256"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 matrix throughput (5.0 POP/s)
+MALL_BYTES = 256 << 20          # Infinity Cache; rotate inputs through > 2x this
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="attn_proj")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain device copy of known size (for HBM counter scaling)")
+    return p.parse_args()
+
+
+class Hip:
+    """hipEvent* through ctypes on an explicit stream."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        self.lib.hipEventRecord(e, stream)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+
+def gpu_bench(args, wl):
+    import numpy as np
+    import torch
+
+    import workloads as wkmod
+    import rotation_w4a4_quantized_convrot_amd as cr
+
+    lib = cr.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, K, N, g = wl.M, wl.K, wl.N, wl.g
+    Kp = wl.Kp
+    tdt = torch.bfloat16 if wl.x_dtype == "bf16" else torch.float32
+    x_np = wkmod.activations(wl)
+    x0 = torch.from_numpy(x_np).to(tdt).to(dev)
+    x_bytes = x0.numel() * x0.element_size()
+    n_x = max(2, -(-2 * MALL_BYTES // x_bytes) + 1)
+    xs_list = [x0] + [x0.clone() for _ in range(n_x - 1)]
+    w = torch.from_numpy(wkmod.weights(wl)).to(tdt).to(dev)
+    b = wkmod.bias(wl)
+    bias = None if b is None else torch.from_numpy(b).to(torch.bfloat16).to(dev)
+    wq, ws = cr.convrot_quant_weight(w, g)
+    n_y = 4
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(n_y)]
+    xq = torch.empty((M, Kp // 2), dtype=torch.uint8, device=dev)
+    xsc = torch.empty((M,), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    dt_code = cr.CONVROT_BF16 if wl.x_dtype == "bf16" else cr.CONVROT_F32
+    x_ptrs = [t.data_ptr() for t in xs_list]
+    y_ptrs = [t.data_ptr() for t in ys]
+    b_ptr = None if bias is None else bias.data_ptr()
+    rq, gemm = lib.convrot_rotate_quant_act, lib.convrot_w4a4_gemm
+    xq_p, xs_p, wq_p, ws_p = xq.data_ptr(), xsc.data_ptr(), wq.data_ptr(), ws.data_ptr()
+
+    def step(i):
+        st = rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream)
+        st |= gemm(xq_p, xs_p, wq_p, ws_p, b_ptr, M, N, Kp, y_ptrs[i % n_y], None, stream)
+        return st
+
+    for i in range(args.warmup):
+        assert step(i) == 0
+    torch.cuda.synchronize()
+
+    hip = Hip()
+    K_steps = args.steps
+    ev = [[hip.event() for _ in range(3)] for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        e = ev[i]
+        hip.record(e[0], stream)
+        rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream)
+        hip.record(e[1], stream)
+        gemm(xq_p, xs_p, wq_p, ws_p, b_ptr, M, N, Kp, y_ptrs[i % n_y], None, stream)
+        hip.record(e[2], stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rq_ms = np.array([hip.ms(e[0], e[1]) for e in ev])
+    gemm_ms = np.array([hip.ms(e[1], e[2]) for e in ev])
+    for e in ev:
+        for x in e:
+            hip.lib.hipEventDestroy(x)
+
+    copy = None
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        copy = {"bytes_each_way": src.numel(), "launches": 3}
+
+    ms_step = (t1 - t0) * 1e3 / K_steps
+    ops = 2.0 * M * N * Kp
+    rq_bytes = M * K * x0.element_size() + M * Kp // 2 + 4 * M
+    rq_us = float(np.mean(rq_ms) * 1e3)
+    gemm_us = float(np.mean(gemm_ms) * 1e3)
+    rq_gbps = rq_bytes / (rq_us * 1e-6) / 1e9
+    gemm_tops = ops / (gemm_us * 1e-6) / 1e12
+    # GEMM algorithmic bytes: packed operands once, scales, bias, bf16 output
+    gemm_bytes = M * Kp // 2 + N * Kp // 2 + 4 * (M + N) + (2 * N if bias is not None else 0) + 2 * M * N
+    return {
+        "ms_per_step": ms_step,
+        "value": ops / (ms_step * 1e-3) / 1e12,
+        "rq_us": rq_us, "rq_us_median": float(np.median(rq_ms) * 1e3), "rq_bytes": rq_bytes,
+        "rq_gbps": rq_gbps, "gemm_us": gemm_us, "gemm_us_median": float(np.median(gemm_ms) * 1e3),
+        "gemm_tops": gemm_tops, "gemm_ops": ops, "gemm_bytes": gemm_bytes,
+        "x_buffers": n_x, "x_buffer_bytes": x_bytes * n_x, "copy_calibration": copy,
+    }
+
+
+def cpu_baseline(args, wl):
+    """The oracle, as it stands, on a bounded row sample of the same workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import workloads as wkmod
+    from oracle import convrot_oracle as O
+
+    x = wkmod.activations(wl)
+    w = wkmod.weights(wl)
+    b = wkmod.bias(wl)
+    refw = O.quantize_weight(w, wl.g)               # offline path, not timed
+    rows = args.cpu_rows or min(wl.M, 1024)
+    xs = x[:rows]
+    t0 = time.perf_counter()
+    r = O.rotate_quantize(xs, wl.g)
+    O.w4a4_linear_from_codes(r["codes"], r["scale"], refw["codes"], refw["scale"], b)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    ops = 2.0 * rows * wl.N * wl.Kp
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {wl.M} rows, all {wl.N} outputs: rotate+quantize + GEMM + "
+                      f"dequant ({dt:.1f} s)",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by rows with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    import workloads as wkmod
+    wl = wkmod.WORKLOADS[args.workload]
+    if wl.N is None:
+        raise SystemExit("the benchmark needs a workload with a weight (N)")
+    r = gpu_bench(args, wl)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl)
+    roof = {"bound": "mfma", "achieved": r["gemm_tops"], "peak": INT8_PEAK_TOPS,
+            "unit": "TFLOP/s", "frac": r["gemm_tops"] / INT8_PEAK_TOPS, "traffic": None,
+            "kernel": "w4a4_gemm_kernel", "launch_us": r["gemm_us"],
+            "algorithmic_ops_per_launch": r["gemm_ops"]}
+    roof_rq = {"bound": "hbm", "achieved": r["rq_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+               "frac": r["rq_gbps"] / HBM_PEAK_GBPS, "traffic": None,
+               "kernel": "rht_quant_kernel", "launch_us": r["rq_us"],
+               "algorithmic_bytes_per_launch": r["rq_bytes"]}
+    out = {
+        "metric": METRIC, "value": r["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "g": wl.g, "Kp": wl.Kp,
+                   "x_dtype": wl.x_dtype, "bias": wl.bias_std is not None,
+                   "x_buffers": r["x_buffers"]},
+        "rotate_quant_GBps": r["rq_gbps"], "rotate_quant_us": r["rq_us"],
+        "gemm_TOPS": r["gemm_tops"], "gemm_us": r["gemm_us"],
+        "roofline": roof, "roofline_rotate_quant": roof_rq, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

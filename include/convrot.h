@@ -1,0 +1,158 @@
+/*
+ * convrot.h -- C ABI of the ConvRot / ConvLinear4bit (rotated W4A4 linear) library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *   [AUTHOR]  ComfyUI issue #14735, comment by the ConvRot author: group-wise rotation by a
+ *             regular Hadamard matrix over non-overlapping windows whose size is a power of 4
+ *             (16, 64, 256, 1024), with zero padding when K is not a multiple of the window.
+ *   [PAPER]   "ConvRot: Rotation-Based Plug-and-Play 4-bit Quantization for Diffusion
+ *             Transformers" (arXiv 2512.03673): Abstract (ConvLinear4bit = rotation,
+ *             quantization, GEMM, dequantization), Fig. 3 (RHT on non-overlapping windows),
+ *             Def. 2.1 / 2.3 (Hadamard and regular Hadamard matrices), Thm. 2.3 (Kronecker
+ *             construction).
+ *   [HSWQ]    HSWQ v2.3.4 release notes, "Mathematical Formulation & Format Layout" ->
+ *             "Hadamard Orthogonal Rotation": W_rot = W H^T, per-row scale = absmax / q_max,
+ *             codes = round(W_rot / scale).
+ *   [KITCHEN] comfy-kitchen PR #65 "Basic convrot int4 support", review comments: the
+ *             integer-only power-of-4 size check and its error text; int4_linear, which
+ *             unpacks row-major int4 operands, accumulates x @ w^T exactly, scales by the
+ *             per-row x scale and per-column w scale, adds the bias and casts last.
+ *
+ * Conventions fixed by this library where the pages are silent:
+ *   - H_g = H4 (x) ... (x) H4 (log4 g factors) with H4 = J - 2I (symmetric, regular, every row
+ *     and column sums to +2); the rotation applied to each window is H_g / sqrt(g).
+ *   - Windows start at column 0.  K' = ceil(K / g) * g; columns K..K'-1 are zero and take
+ *     part in the rotation and in the GEMM (depth K').
+ *   - int4 is symmetric: scale = absmax(rotated row) / 7 (IEEE fp32 division); code =
+ *     clamp(round_half_even(rotated / scale), -8, 7); an all-zero row has scale 0, codes 0.
+ *     The rotated value is the correctly rounded fp32 of the exact rotation; the row scale
+ *     is computed from exact values and is bit-identical to that definition.  Codes are
+ *     computed from an fp32 butterfly and may differ by one from the definition where the
+ *     quotient lies within a few ulp of a rounding tie.
+ *   - Packing: two codes per byte, code 2j in the low nibble of byte j, code 2j+1 in the
+ *     high nibble, two's complement; each row is K'/2 bytes.
+ *   - Output: y = bf16_rne( fp32( fp32( fp32(acc) * x_scale[m] ) * w_scale[n] ) + bias[n] ),
+ *     acc = exact integer sum over K'.  Output is always bf16.
+ *
+ * Memory and threading:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except the host buffer
+ *     of convrot_make_rht.  The library never allocates, frees or retains device memory
+ *     and keeps no mutable global state; calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
+ *     enqueued asynchronously on it; no call synchronises the device or the stream.
+ *   - Every call validates its arguments on the host first and returns a status; on error
+ *     nothing is enqueued and no output is written.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified codes and scales.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define CONVROT_API __attribute__((visibility("default")))
+#else
+#define CONVROT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+    CONVROT_OK = 0,
+    CONVROT_ERR_GROUP = -1,        /* g is not an integer power of 4 (>= 4) */
+    CONVROT_ERR_UNSUPPORTED = -2,  /* a valid power of 4 or shape the kernels do not implement:
+                                      g must be 16, 64, 256 or 1024; the rotate+quantize row
+                                      K' must be at most 16384 (g = 16), 32768 (g = 64, 256)
+                                      or 65536 (g = 1024); the GEMM depth at most
+                                      CONVROT_MAX_KP */
+    CONVROT_ERR_SHAPE = -3,        /* M < 0, N < 0, K < 1, ld < K, or a size that overflows */
+    CONVROT_ERR_NULL = -4,         /* a required pointer is NULL */
+    CONVROT_ERR_DTYPE = -5,        /* unknown dtype code */
+    CONVROT_ERR_ALIGN = -6,        /* a pointer or row stride violates the stated alignment */
+    CONVROT_ERR_WORKSPACE = -7,    /* workspace smaller than convrot_w4a4_workspace_bytes() */
+    CONVROT_ERR_HIP = -8           /* the HIP runtime reported an error at launch */
+};
+
+/* Element type of activation / weight inputs. */
+enum { CONVROT_F32 = 0, CONVROT_BF16 = 1 };
+
+/* Largest padded depth K' any kernel accepts (the GEMM; rotate+quantize rows: see above). */
+#define CONVROT_MAX_KP 65536
+
+/* Human-readable text of a status code (static storage; never NULL). */
+CONVROT_API const char* convrot_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+CONVROT_API int convrot_version(void);
+
+/* K' = ceil(K / g) * g ([AUTHOR]: padding inside the algorithm).
+ * Returns K' >= g, or a negative status: CONVROT_ERR_GROUP if g is not a power of 4,
+ * CONVROT_ERR_SHAPE if K < 1 or K' would overflow. */
+CONVROT_API int64_t convrot_padded_k(int64_t K, int64_t g);
+
+/* Integer-only power-of-4 test ([KITCHEN] review of the size check): 1 if g = 4^k, k >= 1,
+ * else 0.  Accepts every 4^k up to 4^31 (e.g. 2^58 = 4^29). */
+CONVROT_API int convrot_is_power_of_4(int64_t g);
+
+/* Dense regular Hadamard matrix H_g = H4^(x)k, H4 = J - 2I ([PAPER] Def. 2.3, Thm. 2.3),
+ * written row-major into the HOST buffer h[g*g] (fp32).  normalized = 0: entries +-1;
+ * normalized != 0: entries +-1/sqrt(g) (exact powers of two).  For reference and tests;
+ * the GPU path never materialises H.  Errors: CONVROT_ERR_GROUP, CONVROT_ERR_NULL,
+ * CONVROT_ERR_UNSUPPORTED if g > 4096. */
+CONVROT_API int convrot_make_rht(int64_t g, float* h, int32_t normalized);
+
+/* Online activation path ([AUTHOR]; [PAPER] Abstract, Fig. 3): for each of the M rows of x
+ * (row stride ldx elements), zero-pad to K', rotate every window of g columns by H_g/sqrt(g),
+ * take the per-row absmax scale and quantize to int4.
+ *   x        device, dtype x_dtype, [M][ldx] with ldx >= K; any alignment of the element type
+ *   xq       device, uint8 [M][K'/2] packed codes (layout above); 16-byte aligned
+ *   xs       device, fp32 [M] per-row scales; 4-byte aligned
+ *   xrot     device, fp32 [M][K'] rotated activations, or NULL (debug output)
+ * M = 0 is a no-op.  Errors: GROUP, UNSUPPORTED, SHAPE, NULL, DTYPE, ALIGN, HIP. */
+CONVROT_API int convrot_rotate_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             int64_t g, uint8_t* xq, float* xs, float* xrot, void* stream);
+
+/* Offline weight path ([HSWQ] "Hadamard Orthogonal Rotation", per output channel): the same
+ * operation on the N rows of w [N][K] (row stride K): wq uint8 [N][K'/2] (16-byte aligned),
+ * ws fp32 [N].  Called once per layer; not on the forward path. */
+CONVROT_API int convrot_quant_weight(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t g,
+                         uint8_t* wq, float* ws, void* stream);
+
+/* W4A4 GEMM with fused dequantization ([KITCHEN] int4_linear semantics; int8 matrix cores):
+ *   y[m][n] = bf16( fp32(fp32(fp32(sum_k qx[m][k] qw[n][k]) * xs[m]) * ws[n]) + bias[n] )
+ *   xq [M][Kp/2], wq [N][Kp/2] packed int4 (16-byte aligned), xs fp32 [M], ws fp32 [N],
+ *   bias bf16 [N] or NULL, y bf16 [M][N] row-major (4-byte aligned).
+ *   Kp must be a positive multiple of 16 and <= CONVROT_MAX_KP.
+ *   acc_dbg: int32 [M][N] (16-byte aligned) or NULL; when set, the exact integer sums are
+ *   written there as well (debug / bit-exactness checks).
+ * M = 0 or N = 0 is a no-op.  Errors: SHAPE, NULL, ALIGN, UNSUPPORTED, HIP. */
+CONVROT_API int convrot_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                      const void* bias, int64_t M, int64_t N, int64_t Kp, void* y,
+                      int32_t* acc_dbg, void* stream);
+
+/* Bytes of device workspace convrot_w4a4_linear needs: packed codes M*K'/2 and scales 4*M,
+ * each rounded up to 256 bytes.  Returns 0 for an invalid g or shape. */
+CONVROT_API size_t convrot_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t g);
+
+/* The ConvLinear4bit forward pass ([PAPER] Abstract, Fig. 3): rotate + quantize x [M][K]
+ * (row stride K, dtype x_dtype) into the workspace, then the W4A4 GEMM against the offline
+ * weights wq [N][K'/2] / ws [N] (from convrot_quant_weight with the same g and K) with the
+ * dequant epilogue, writing y bf16 [M][N].  bias bf16 [N] or NULL.  The workspace (device,
+ * 256-byte aligned, ws_bytes >= convrot_w4a4_workspace_bytes(M, K, g)) holds the packed
+ * activation codes and scales afterwards.  Two kernels are enqueued on `stream`.
+ * M = 0 or N = 0 is a no-op.  Errors: GROUP, UNSUPPORTED, SHAPE, NULL, DTYPE, ALIGN,
+ * WORKSPACE, HIP. */
+CONVROT_API int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t g,
+                        const uint8_t* wq, const float* ws, int64_t N, const void* bias,
+                        void* y, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

@@ -1,0 +1,19 @@
+"""MI355X-native ConvRot / ConvLinear4bit (rotated W4A4 linear) for gfx950.
+
+The compute path is libconvrot.so (hand-written HIP kernels behind a C ABI, declared in
+include/convrot.h); this package is its thin Python binding plus the ConvLinear4bit module.
+"""
+from ._lib import (  # noqa: F401
+    CONVROT_BF16, CONVROT_F32, CONVROT_MAX_KP, ConvRotError, LIB_PATH, SIGNATURES,
+    convrot_is_power_of_4, convrot_make_rht, convrot_padded_k, convrot_quant_weight,
+    convrot_rotate_quant_act, convrot_status_string, convrot_version, convrot_w4a4_gemm,
+    convrot_w4a4_linear, convrot_w4a4_workspace_bytes, load_library,
+)
+from .linear import ConvLinear4bit  # noqa: F401
+
+__all__ = [
+    "ConvLinear4bit", "ConvRotError", "load_library", "convrot_status_string", "convrot_version",
+    "convrot_padded_k", "convrot_is_power_of_4", "convrot_make_rht", "convrot_rotate_quant_act",
+    "convrot_quant_weight", "convrot_w4a4_gemm", "convrot_w4a4_workspace_bytes",
+    "convrot_w4a4_linear",
+]

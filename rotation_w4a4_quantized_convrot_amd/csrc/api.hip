@@ -1,0 +1,196 @@
+// C ABI of libconvrot: host-side argument validation, status codes, launches.
+// Semantics and citations: include/convrot.h.
+#include "convrot.h"
+#include "convrot_internal.h"
+
+namespace {
+
+int pow4_exponent(int64_t g) {
+  // Integer-only power-of-4 test (comfy-kitchen PR #65 review of the size check).
+  if (g < 4 || (g & (g - 1)) != 0) return -1;
+  const int bits = 63 - __builtin_clzll((unsigned long long)g);
+  return (bits % 2 == 0) ? bits / 2 : -1;
+}
+
+bool kernel_group(int64_t g) { return g == 16 || g == 64 || g == 256 || g == 1024; }
+
+// Longest padded row the rotate+quantize kernel holds on chip: 16 waves x 64 lanes x the
+// elements per lane of its window layout (16 for g = 16, 32 for g = 64 and 256, 64 for 1024).
+int64_t max_row_kp(int64_t g) { return g == 16 ? 16384 : g == 1024 ? 65536 : 32768; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int elem_size(int32_t dtype) { return dtype == CONVROT_F32 ? 4 : dtype == CONVROT_BF16 ? 2 : 0; }
+
+// Widest power-of-two vector width (<= 16 bytes) that divides both the base address and
+// the row stride in bytes.
+int vector_width(const void* x, int64_t ld_bytes) {
+  int v = 16;
+  while (v > 1 && (!aligned(x, (size_t)v) || (ld_bytes % v) != 0)) v /= 2;
+  return v;
+}
+
+int check_group(int64_t g) {
+  if (pow4_exponent(g) < 0) return CONVROT_ERR_GROUP;
+  if (!kernel_group(g)) return CONVROT_ERR_UNSUPPORTED;
+  return CONVROT_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_HIP; }
+
+// Validates a rotate+quantize call; on success *kp_out = K'.
+int validate_rq(const void* x, int32_t dtype, int64_t M, int64_t K, int64_t ldx, int64_t g,
+                const uint8_t* q, const float* s, const float* xrot, int64_t* kp_out) {
+  int st = check_group(g);
+  if (st != CONVROT_OK) return st;
+  if (elem_size(dtype) == 0) return CONVROT_ERR_DTYPE;
+  if (M < 0 || K < 1 || ldx < K || M > INT32_MAX || ldx > (INT64_MAX / 8) / (M > 0 ? M : 1))
+    return CONVROT_ERR_SHAPE;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return (int)kp;
+  if (kp > max_row_kp(g)) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0) {
+    *kp_out = kp;
+    return CONVROT_OK;
+  }
+  if (x == nullptr || q == nullptr || s == nullptr) return CONVROT_ERR_NULL;
+  if (!aligned(x, (size_t)elem_size(dtype)) || !aligned(q, 16) || !aligned(s, 4) ||
+      (xrot != nullptr && !aligned(xrot, 16)))
+    return CONVROT_ERR_ALIGN;
+  *kp_out = kp;
+  return CONVROT_OK;
+}
+
+int validate_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                  const void* bias, int64_t M, int64_t N, int64_t Kp, const void* y,
+                  const int32_t* acc_dbg) {
+  if (M < 0 || N < 0 || Kp < 16 || (Kp % 16) != 0 || M > INT32_MAX || N > INT32_MAX)
+    return CONVROT_ERR_SHAPE;
+  if (Kp > CONVROT_MAX_KP) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (xq == nullptr || xs == nullptr || wq == nullptr || ws == nullptr || y == nullptr)
+    return CONVROT_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xs, 4) || !aligned(ws, 4) ||
+      !aligned(y, 4) || (bias != nullptr && !aligned(bias, 2)) ||
+      (acc_dbg != nullptr && !aligned(acc_dbg, 16)))
+    return CONVROT_ERR_ALIGN;
+  return CONVROT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* convrot_status_string(int status) {
+  switch (status) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_ERR_GROUP: return "group size is not a power of 4 (>= 4)";
+    case CONVROT_ERR_UNSUPPORTED:
+      return "unsupported: group size must be 16, 64, 256 or 1024, and K' at most 16384 "
+             "(g = 16), 32768 (g = 64, 256) or 65536 (g = 1024)";
+    case CONVROT_ERR_SHAPE: return "invalid shape (M, N >= 0, K >= 1, ld >= K, no overflow)";
+    case CONVROT_ERR_NULL: return "a required pointer is NULL";
+    case CONVROT_ERR_DTYPE: return "unknown dtype code";
+    case CONVROT_ERR_ALIGN: return "pointer or row stride violates the required alignment";
+    case CONVROT_ERR_WORKSPACE: return "workspace too small";
+    case CONVROT_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int convrot_version(void) { return 100; }
+
+int convrot_is_power_of_4(int64_t g) { return pow4_exponent(g) >= 0 ? 1 : 0; }
+
+int64_t convrot_padded_k(int64_t K, int64_t g) {
+  if (pow4_exponent(g) < 0) return CONVROT_ERR_GROUP;
+  if (K < 1 || K > INT64_MAX - g) return CONVROT_ERR_SHAPE;
+  return ((K + g - 1) / g) * g;
+}
+
+int convrot_make_rht(int64_t g, float* h, int32_t normalized) {
+  const int k = pow4_exponent(g);
+  if (k < 0) return CONVROT_ERR_GROUP;
+  if (g > 4096) return CONVROT_ERR_UNSUPPORTED;
+  if (h == nullptr) return CONVROT_ERR_NULL;
+  // Closed form of H4^(x)k with H4 = J - 2I: the entry is -1 to the number of base-4 digits
+  // in which i and j agree.
+  const float mag = normalized ? 1.0f / float(1 << k) : 1.0f;
+  for (int64_t i = 0; i < g; ++i)
+    for (int64_t j = 0; j < g; ++j) {
+      int equal = 0;
+      for (int t = 0; t < k; ++t) equal += (((i >> (2 * t)) & 3) == ((j >> (2 * t)) & 3));
+      h[i * g + j] = (equal & 1) ? -mag : mag;
+    }
+  return CONVROT_OK;
+}
+
+int convrot_rotate_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                             int64_t g, uint8_t* xq, float* xs, float* xrot, void* stream) {
+  int64_t kp = 0;
+  const int st = validate_rq(x, x_dtype, M, K, ldx, g, xq, xs, xrot, &kp);
+  if (st != CONVROT_OK || M == 0) return st;
+  const int vec = vector_width(x, ldx * elem_size(x_dtype));
+  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp, vec, xq, xs,
+                                                xrot, static_cast<hipStream_t>(stream)));
+}
+
+int convrot_quant_weight(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t g,
+                         uint8_t* wq, float* ws, void* stream) {
+  return convrot_rotate_quant_act(w, w_dtype, N, K, K, g, wq, ws, nullptr, stream);
+}
+
+int convrot_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                      const void* bias, int64_t M, int64_t N, int64_t Kp, void* y,
+                      int32_t* acc_dbg, void* stream) {
+  const int st = validate_gemm(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg);
+  if (st != CONVROT_OK || M == 0 || N == 0) return st;
+  const int vec = ((Kp / 2) % 16 == 0) ? 16 : 8;
+  return status_of(convrot::launch_w4a4_gemm(xq, xs, wq, ws, static_cast<const uint16_t*>(bias),
+                                             M, N, Kp, static_cast<uint16_t*>(y), acc_dbg, vec,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t convrot_w4a4_workspace_bytes(int64_t M, int64_t K, int64_t g) {
+  if (M < 0 || M > INT32_MAX) return 0;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return 0;
+  return round256((size_t)M * (size_t)(kp / 2)) + round256((size_t)M * 4);
+}
+
+int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t g,
+                        const uint8_t* wq, const float* ws, int64_t N, const void* bias, void* y,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_group(g);
+  if (st != CONVROT_OK) return st;
+  if (elem_size(x_dtype) == 0) return CONVROT_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 1 || M > INT32_MAX || N > INT32_MAX) return CONVROT_ERR_SHAPE;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return (int)kp;
+  if (kp > max_row_kp(g)) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (x == nullptr || wq == nullptr || ws == nullptr || y == nullptr || workspace == nullptr)
+    return CONVROT_ERR_NULL;
+  if (!aligned(workspace, 256)) return CONVROT_ERR_ALIGN;
+  if (ws_bytes < convrot_w4a4_workspace_bytes(M, K, g)) return CONVROT_ERR_WORKSPACE;
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(xq + round256((size_t)M * (size_t)(kp / 2)));
+  int64_t kp_rq = 0;
+  st = validate_rq(x, x_dtype, M, K, K, g, xq, xs, nullptr, &kp_rq);
+  if (st != CONVROT_OK) return st;
+  st = validate_gemm(xq, xs, wq, ws, bias, M, N, kp, y, nullptr);
+  if (st != CONVROT_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int vec = vector_width(x, K * elem_size(x_dtype));
+  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, vec, xq, xs,
+                                              nullptr, s);
+  if (e != hipSuccess) return CONVROT_ERR_HIP;
+  const int gvec = ((kp / 2) % 16 == 0) ? 16 : 8;
+  e = convrot::launch_w4a4_gemm(xq, xs, wq, ws, static_cast<const uint16_t*>(bias), M, N, kp,
+                                static_cast<uint16_t*>(y), nullptr, gvec, s);
+  return status_of(e);
+}
+
+}  // extern "C"

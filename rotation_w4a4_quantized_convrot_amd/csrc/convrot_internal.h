@@ -1,0 +1,34 @@
+// Internal declarations shared by the HIP kernels and the C ABI of libconvrot.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+// Launches the fused pad + group-wise RHT + per-row absmax + int4 quantize + pack kernel
+// on rows [0, M) of x (row stride ldx elements).  g in {16, 64, 256, 1024}; Kp = K' <= 65536.
+// x_dtype: 0 = fp32, 1 = bf16.  vec_bytes: widest aligned vector load (2, 4, 8 or 16 bytes).
+hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               int g, int64_t Kp, int vec_bytes, uint8_t* q, float* s,
+                               float* xrot, hipStream_t stream);
+
+// Launches the W4A4 GEMM with the fused dequant epilogue.  vec_bytes: 16 when the packed
+// row stride Kp/2 is a multiple of 16 bytes, else 8.
+hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq,
+                            const float* ws, const uint16_t* bias, int64_t M, int64_t N,
+                            int64_t Kp, uint16_t* y, int32_t* acc_dbg, int vec_bytes,
+                            hipStream_t stream);
+
+// Small launch helper that returns the launch status instead of relying on hipGetLastError.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                                hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+  return [&](KArgs... typed) {
+    void* argv[] = {(void*)&typed...};
+    return hipLaunchKernel((const void*)kernel, grid, block, argv, shmem, stream);
+  }(static_cast<KArgs>(args)...);
+}
+
+}  // namespace convrot
