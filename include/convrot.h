@@ -68,8 +68,8 @@ enum {
     CONVROT_ERR_UNSUPPORTED = -2,  /* a valid power of 4 or shape the kernels do not implement:
                                       g must be 16, 64, 256 or 1024; the rotate+quantize row
                                       K' must be at most 16384 (g = 16), 32768 (g = 64, 256)
-                                      or 65536 (g = 1024); the GEMM depth at most
-                                      CONVROT_MAX_KP */
+                                      or 61440 (g = 1024; 32768 for fp32 input); the GEMM
+                                      depth at most CONVROT_MAX_KP */
     CONVROT_ERR_SHAPE = -3,        /* M < 0, N < 0, K < 1, ld < K, or a size that overflows */
     CONVROT_ERR_NULL = -4,         /* a required pointer is NULL */
     CONVROT_ERR_DTYPE = -5,        /* unknown dtype code */

@@ -14,9 +14,15 @@ int pow4_exponent(int64_t g) {
 
 bool kernel_group(int64_t g) { return g == 16 || g == 64 || g == 256 || g == 1024; }
 
-// Longest padded row the rotate+quantize kernel holds on chip: 16 waves x 64 lanes x the
-// elements per lane of its window layout (16 for g = 16, 32 for g = 64 and 256, 64 for 1024).
-int64_t max_row_kp(int64_t g) { return g == 16 ? 16384 : g == 1024 ? 65536 : 32768; }
+// Longest padded row the rotate+quantize kernel holds on chip: at most 16 waves x 64 lanes x
+// the elements per lane of its window layout (16 for g = 16, 32 for g = 64 and 256, 64 for
+// 1024), and the workgroup's LDS staging within 160 KiB (g = 1024: 15 waves for bf16, 8 for
+// fp32 inputs).
+int64_t max_row_kp(int64_t g, int32_t dtype) {
+  if (g == 16) return 16384;
+  if (g == 1024) return dtype == CONVROT_F32 ? 32768 : 61440;
+  return 32768;
+}
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -50,7 +56,7 @@ int validate_rq(const void* x, int32_t dtype, int64_t M, int64_t K, int64_t ldx,
     return CONVROT_ERR_SHAPE;
   const int64_t kp = convrot_padded_k(K, g);
   if (kp < 0) return (int)kp;
-  if (kp > max_row_kp(g)) return CONVROT_ERR_UNSUPPORTED;
+  if (kp > max_row_kp(g, dtype)) return CONVROT_ERR_UNSUPPORTED;
   if (M == 0) {
     *kp_out = kp;
     return CONVROT_OK;
@@ -89,7 +95,7 @@ const char* convrot_status_string(int status) {
     case CONVROT_ERR_GROUP: return "group size is not a power of 4 (>= 4)";
     case CONVROT_ERR_UNSUPPORTED:
       return "unsupported: group size must be 16, 64, 256 or 1024, and K' at most 16384 "
-             "(g = 16), 32768 (g = 64, 256) or 65536 (g = 1024)";
+             "(g = 16), 32768 (g = 64, 256) or 61440 (g = 1024; 32768 for fp32 input)";
     case CONVROT_ERR_SHAPE: return "invalid shape (M, N >= 0, K >= 1, ld >= K, no overflow)";
     case CONVROT_ERR_NULL: return "a required pointer is NULL";
     case CONVROT_ERR_DTYPE: return "unknown dtype code";
@@ -169,7 +175,7 @@ int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
   if (M < 0 || N < 0 || K < 1 || M > INT32_MAX || N > INT32_MAX) return CONVROT_ERR_SHAPE;
   const int64_t kp = convrot_padded_k(K, g);
   if (kp < 0) return (int)kp;
-  if (kp > max_row_kp(g)) return CONVROT_ERR_UNSUPPORTED;
+  if (kp > max_row_kp(g, x_dtype)) return CONVROT_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return CONVROT_OK;
   if (x == nullptr || wq == nullptr || ws == nullptr || y == nullptr || workspace == nullptr)
     return CONVROT_ERR_NULL;

@@ -29,6 +29,8 @@
 //   * Packed codes go through LDS so every lane writes 8-32 contiguous bytes.
 #include "convrot_internal.h"
 
+#include <algorithm>
+
 namespace convrot {
 namespace {
 
@@ -86,15 +88,11 @@ __device__ __forceinline__ void rad4_split(float& a, float& b) {
   b = __builtin_fmaf(0.5f, s, -b);
 }
 
+// Radix-4 stages for digits 1..k-1 of the window held by a unit.
 template <int G>
 __device__ __forceinline__ void rotate_window(float (&v)[Geo<G>::E]) {
   constexpr int C = Geo<G>::E / 8;
-  // digit 0: element bits 0,1 of every chunk
-#pragma unroll
-  for (int r = 0; r < C; ++r) {
-    rad4(v[8 * r + 0], v[8 * r + 1], v[8 * r + 2], v[8 * r + 3]);
-    rad4(v[8 * r + 4], v[8 * r + 5], v[8 * r + 6], v[8 * r + 7]);
-  }
+  // digit 0 (element bits 0, 1) is applied while decoding the chunk (decode_stage0)
   // digit 1: element bit 2 (register) and position bit 3
   if constexpr (G == 16) {
 #pragma unroll
@@ -144,108 +142,206 @@ __device__ __forceinline__ float unit_max(float m) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Loads the 8 consecutive elements at p (all in bounds) with loads of VEC bytes.
+// ---------------------------------------------------------------- buffer access
+// Buffer resources: every access carries a 32-bit byte offset from a per-block scalar base,
+// and dwords past num_records read as zero (stores past it are dropped), which provides the
+// zero padding past the end of x, masks rows past M and retires idle lanes for free.
+constexpr uint32_t kRsrcFlags = 0x00020000u;  // raw 32-bit dword buffer, gfx9 family
+constexpr uint32_t kOob = 0x80000000u;        // past every num_records (<= 0x7FFFFFF0), with room
+                                              // for the +16 of a second load
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long bytes) {
+  const int n = bytes <= 0 ? 0 : bytes >= 0x7FFFFFF0L ? 0x7FFFFFF0 : int(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcFlags);
+}
+
+template <typename TIn> struct ES_WORDS { static constexpr int value = sizeof(TIn) == 2 ? 2 : 4; };
+template <typename TIn> struct RawChunk;
+template <> struct RawChunk<uint16_t> { uint4 w; };
+template <> struct RawChunk<float> { uint4 w0, w1; };
+
+// Loads one chunk at byte offset off with loads of VEC bytes (the widest the row alignment
+// allows); VEC = 2 reads bf16 elements one by one.
 template <typename TIn, int VEC>
-__device__ __forceinline__ void load_chunk(const TIn* __restrict__ p, float* __restrict__ out) {
-  if constexpr (sizeof(TIn) == 2) {
-    const uint16_t* h = reinterpret_cast<const uint16_t*>(p);
-    uint32_t w[4];
-    if constexpr (VEC >= 16) {
-      const uint4 t = *reinterpret_cast<const uint4*>(h);
-      w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
-    } else if constexpr (VEC == 8) {
-      const uint2 a = reinterpret_cast<const uint2*>(h)[0];
-      const uint2 b = reinterpret_cast<const uint2*>(h)[1];
-      w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y;
-    } else if constexpr (VEC == 4) {
+__device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rs, uint32_t off, RawChunk<TIn>& c) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  uint32_t w[2 * ES_WORDS<TIn>::value];
+  constexpr int NW = 2 * ES_WORDS<TIn>::value;  // dwords per chunk: 4 (bf16) or 8 (fp32)
+  if constexpr (VEC == 16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(h)[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = uint32_t(h[2 * i]) | (uint32_t(h[2 * i + 1]) << 16);
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 t = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, 0, 0));
+      w[4 * i] = t.x; w[4 * i + 1] = t.y; w[4 * i + 2] = t.z; w[4 * i + 3] = t.w;
     }
+  } else if constexpr (VEC == 8) {
+#pragma unroll
+    for (int i = 0; i < NW / 2; ++i) {
+      const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off + 8 * i, 0, 0));
+      w[2 * i] = t.x; w[2 * i + 1] = t.y;
+    }
+  } else if constexpr (VEC == 4) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 4 * i, 0, 0);
+  } else {
+    static_assert(sizeof(TIn) == 2, "2-byte loads are for bf16 only");
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t lo = __builtin_bit_cast(unsigned short, __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4 * i, 0, 0));
+      const uint32_t hi = __builtin_bit_cast(unsigned short, __builtin_amdgcn_raw_buffer_load_b16(rs, off + 4 * i + 2, 0, 0));
+      w[i] = lo | (hi << 16);
+    }
+  }
+  if constexpr (sizeof(TIn) == 2) {
+    c.w = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    c.w0 = make_uint4(w[0], w[1], w[2], w[3]);
+    c.w1 = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// Zeroes the elements of a chunk starting at column col that lie at or past column K.
+template <typename TIn>
+__device__ __forceinline__ void mask_tail(RawChunk<TIn>& c, int col, int K) {
+  if constexpr (sizeof(TIn) == 2) {
+    uint32_t w[4] = {c.w.x, c.w.y, c.w.z, c.w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(w[i] << 16);
-      out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      const uint32_t keep = (col + 2 * i < K ? 0xFFFFu : 0u) | (col + 2 * i + 1 < K ? 0xFFFF0000u : 0u);
+      w[i] &= keep;
+    }
+    c.w = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint32_t w[8] = {c.w0.x, c.w0.y, c.w0.z, c.w0.w, c.w1.x, c.w1.y, c.w1.z, c.w1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = col + i < K ? w[i] : 0u;
+    c.w0 = make_uint4(w[0], w[1], w[2], w[3]);
+    c.w1 = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// v_dot2_f32_bf16 (VOP3P): D = w.lo * c.lo + w.hi * c.hi + acc, with the bf16 pair coefficient
+// in an SGPR.  Written as an ALU-only asm statement because the compiler otherwise selects the
+// accumulate-in-place VOP2 form and copies the shared accumulator for every use.
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t coef, float acc) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(w), "s"(coef), "v"(acc));
+  return d;
+}
+__device__ __forceinline__ float dot2_zero(uint32_t w, uint32_t coef) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(w), "s"(coef));
+  return d;
+}
+
+// Decodes a raw chunk into 8 fp32 values and applies radix-4 stage 0 (position bits 0, 1).
+// For bf16 the decode is folded into the stage with v_dot2_f32_bf16: S/2 from two dot
+// products with (1/2, 1/2), then S/2 - x_i with (-1, 0) / (0, -1).  Its error is bounded by
+// a few u times the sum of the term magnitudes (not correctly rounded), which the candidate
+// slack below allows for.
+template <typename TIn>
+__device__ __forceinline__ void decode_stage0(const RawChunk<TIn>& c, float* __restrict__ v) {
+  if constexpr (sizeof(TIn) == 2) {
+    constexpr uint32_t kHalf = 0x3F003F00u, kNegLo = 0x0000BF80u, kNegHi = 0xBF800000u;
+    const uint32_t w[4] = {c.w.x, c.w.y, c.w.z, c.w.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t a = w[2 * h], b = w[2 * h + 1];
+      const float hs = dot2(b, kHalf, dot2_zero(a, kHalf));
+      v[4 * h + 0] = dot2(a, kNegLo, hs);
+      v[4 * h + 1] = dot2(a, kNegHi, hs);
+      v[4 * h + 2] = dot2(b, kNegLo, hs);
+      v[4 * h + 3] = dot2(b, kNegHi, hs);
     }
   } else {
-    const float* f = reinterpret_cast<const float*>(p);
-    if constexpr (VEC >= 16) {
-      const float4 a = reinterpret_cast<const float4*>(f)[0];
-      const float4 b = reinterpret_cast<const float4*>(f)[1];
-      out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
-      out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
-    } else if constexpr (VEC == 8) {
+    const uint32_t w[8] = {c.w0.x, c.w0.y, c.w0.z, c.w0.w, c.w1.x, c.w1.y, c.w1.z, c.w1.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float2 a = reinterpret_cast<const float2*>(f)[i];
-        out[2 * i] = a.x; out[2 * i + 1] = a.y;
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+    rad4(v[0], v[1], v[2], v[3]);
+    rad4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <typename TIn>
+__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t rs, uint32_t elem_off) {
+  if constexpr (sizeof(TIn) == 2) {
+    const uint32_t h = __builtin_bit_cast(unsigned short,
+        __builtin_amdgcn_raw_buffer_load_b16(rs, elem_off * 2u, 0, 0));
+    return bf16_bits_to_f32(h);
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, elem_off * 4u, 0, 0));
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, uint32_t(b), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, uint32_t(b >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(b), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(b >> 32), lane);
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+// Exact |fp32(y[p])| of position p of a window whose raw inputs (bf16 or fp32, in position
+// order, zero past column K) sit in LDS at win, computed by the whole wavefront in fp64:
+// sum_t (-1)^(#equal base-4 digits of p and t) x[t], times 2^-k.  Lane l sums T consecutive
+// positions; the 16 lanes of a row are combined with DPP and the four rows through readlane.
+// The fp64 sums are exact for bf16 windows whose exponent spread is below 35 binades.
+template <int G, typename TIn>
+__device__ __forceinline__ float exact_rotated_abs(const TIn* win, int p, int lane) {
+  constexpr int KD = Geo<G>::KD;
+  constexpr int kDigitMask = 0x55555 & ((1 << (2 * KD)) - 1);
+  constexpr int T = (G + 63) / 64;   // consecutive positions per lane
+  double acc = 0.0;
+  if (lane * T < G) {
+    float xv[T];
+    if constexpr (sizeof(TIn) == 2) {
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(win) + lane * T;
+      if constexpr (T == 16) {
+        const uint4 a = reinterpret_cast<const uint4*>(h)[0], c = reinterpret_cast<const uint4*>(h)[1];
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          xv[2 * i] = __uint_as_float(w[i] << 16);
+          xv[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+      } else if constexpr (T == 4) {
+        const uint2 a = *reinterpret_cast<const uint2*>(h);
+        xv[0] = __uint_as_float(a.x << 16); xv[1] = __uint_as_float(a.x & 0xFFFF0000u);
+        xv[2] = __uint_as_float(a.y << 16); xv[3] = __uint_as_float(a.y & 0xFFFF0000u);
+      } else {
+#pragma unroll
+        for (int i = 0; i < T; ++i) xv[i] = bf16_bits_to_f32(h[i]);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = f[e];
+      for (int i = 0; i < T; ++i) xv[i] = reinterpret_cast<const float*>(win)[lane * T + i];
+    }
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const int d = p ^ (lane * T + i);
+      const int differing = __builtin_popcount((d | (d >> 1)) & kDigitMask);
+      acc += ((KD - differing) & 1) ? -(double)xv[i] : (double)xv[i];
     }
   }
-}
-
-// Elements col..col+7 of a row whose chunk crosses or lies beyond column K: columns >= K
-// are the zero padding of the last window.
-template <typename TIn>
-__device__ __forceinline__ void load_chunk_tail(const TIn* __restrict__ row, int col, int K,
-                                                float* __restrict__ out) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float val = 0.0f;
-    if (col + e < K) {
-      if constexpr (sizeof(TIn) == 2)
-        val = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row)[col + e]);
-      else
-        val = reinterpret_cast<const float*>(row)[col + e];
-    }
-    out[e] = val;
-  }
-}
-
-template <typename TIn>
-__device__ __forceinline__ double load_elem_f64(const TIn* __restrict__ row, int col) {
-  if constexpr (sizeof(TIn) == 2)
-    return (double)bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(row)[col]);
-  else
-    return (double)reinterpret_cast<const float*>(row)[col];
-}
-
-// Exact |fp32(y[p])| of position p of window j, computed by the whole wavefront in fp64
-// from the raw inputs: sum_t (-1)^(#equal base-4 digits of p and t) x[j g + t], times 2^-k.
-template <int G, typename TIn>
-__device__ float exact_rotated_abs(const TIn* __restrict__ row, int K, int j, int p, int lane) {
-  constexpr int KD = Geo<G>::KD;
-  constexpr int kDigitMask = 0x55555 & ((1 << (2 * KD)) - 1);
-  constexpr int T = (G + 63) / 64;
-  double xv[T];
-#pragma unroll
-  for (int i = 0; i < T; ++i) {  // all loads issued before any use
-    const int t = 64 * i + lane, col = j * G + t;
-    const bool ok = t < G && col < K;
-    xv[i] = load_elem_f64(row, ok ? col : 0);
-    if (!ok) xv[i] = 0.0;
-  }
-  double acc = 0.0;
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const int d = p ^ (64 * i + lane);
-    const int differing = __builtin_popcount((d | (d >> 1)) & kDigitMask);
-    acc += ((KD - differing) & 1) ? -xv[i] : xv[i];
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  acc = __shfl(acc, 0);
-  return fabsf((float)(acc * (1.0 / double(1 << KD))));
+  acc += dpp_f64<kDppXor1>(acc);
+  acc += dpp_f64<kDppXor2>(acc);
+  acc += dpp_f64<kDppXor7>(acc);
+  acc += dpp_f64<kDppXor15>(acc);
+  const double sum = (readlane_f64(acc, 0) + readlane_f64(acc, 16)) +
+                     (readlane_f64(acc, 32) + readlane_f64(acc, 48));
+  return fabsf((float)(sum * (1.0 / double(1 << KD))));
 }
 
 // Relative slack of the candidate test: 8 (14 k sqrt(g) + 2) u with u = 2^-24.  A rigorous
-// bound on |fp32 butterfly - fp32(exact)| is (6 k sqrt(g) + 1) u max|y|; twice that separates
-// the true argmax from the fp32 max, and the constant here is a further factor > 2 above it.
+// bound on |fp32 butterfly - fp32(exact)| is (6 k sqrt(g) + 1) u max|y| with correctly rounded
+// operations and (6 k + 12) sqrt(g) u max|y| with the v_dot2 first stage; twice that separates
+// the true argmax from the fp32 max, and the constant here stays a factor > 5 above it.
 template <int G>
 __device__ __forceinline__ float candidate_slack() {
   constexpr int KD = Geo<G>::KD;
@@ -253,125 +349,161 @@ __device__ __forceinline__ float candidate_slack() {
   return float(8 * (14 * KD * sqrt_g + 2)) * 5.9604644775390625e-8f;
 }
 
+// Persistent workgroups: each one owns `waves` wavefronts holding R rows x W windows (one
+// window per unit of L lanes) and walks the row blocks b = blockIdx.x, + gridDim.x, ...,
+// prefetching block b + gridDim.x into registers while block b is processed.  One workgroup
+// barrier per block: per-row maxima meet in LDS through atomics on four rotating buffers;
+// the row scale (which needs the exact maximum) is stored one iteration later.
 template <int G, typename TIn, int VEC>
 __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__ x, int M, int K,
                                                          long ldx, int Kp, int W, int R,
-                                                         uint8_t* __restrict__ q,
+                                                         int nblocks, uint8_t* __restrict__ q,
                                                          float* __restrict__ s,
                                                          float* __restrict__ xrot) {
   constexpr int L = Geo<G>::L, E = Geo<G>::E, C = E / 8, U = 64 / L;
+  constexpr int ES = sizeof(TIn);
+  constexpr int kWinBytes = G / 2, kLaneBytes = E / 2;
   extern __shared__ uint32_t smem[];
-  uint32_t* row_max = smem;        // [R] fp32 max of the butterfly values (as bits)
-  uint32_t* row_exact = smem + R;  // [R] exact fp32 absmax (as bits)
-  uint8_t* stage = reinterpret_cast<uint8_t*>(smem + ((2 * R + 3) & ~3));
+  uint32_t* red = smem;  // [4 buffers][2 (fp32 max, exact max)][R], float bits
+  const int nwaves = blockDim.x >> 6;
+  uint8_t* stage = reinterpret_cast<uint8_t*>(smem + ((8 * R + 3) & ~3));  // packed windows
+  uint8_t* rawwin = stage + nwaves * U * kWinBytes;  // raw input windows, position order
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = lane / L, lu = lane % L;
   const int slot = wave * U + unit;
   const int rloc = slot / W, j = slot - rloc * W;
-  const long m = (long)blockIdx.x * R + rloc;
-  const bool active = rloc < R && m < M;
+  const bool slot_used = rloc < R;
 
-  for (int i = tid; i < 2 * R; i += blockDim.x) smem[i] = 0u;
-
-  // Whole chunks are loaded unconditionally (from an in-bounds address) so every load is
-  // in flight at once; chunks that cross or pass column K, and idle lanes, are patched after.
-  float v[E];
-  const TIn* xr = x + (active ? m : 0) * ldx;
-  bool whole[C];
-  int cols[C];
+  // Lane-constant byte offsets inside a block: input chunks (out of range for padding chunks
+  // and idle slots), the packed output bytes of this lane, and the rotated-value debug output.
+  uint32_t voff[C];
+  bool partial = false;
 #pragma unroll
   for (int r = 0; r < C; ++r) {
-    cols[r] = j * G + 8 * chunk_of<G>(lu, r);
-    whole[r] = active && cols[r] + 8 <= K;
+    const int col = j * G + 8 * chunk_of<G>(lu, r);
+    voff[r] = (slot_used && col < K) ? uint32_t((rloc * ldx + col) * ES) : kOob;
+    partial |= slot_used && col < K && col + 8 > K;
   }
-  if (K >= 8) {  // uniform: columns 0..7 of a row exist, so they are a safe load address
+  const bool any_partial = __ballot(partial) != 0;
+  const uint32_t qoff = slot_used ? uint32_t(rloc * (Kp / 2) + j * kWinBytes + lu * kLaneBytes) : kOob;
+  const long blk_in = long(R) * ldx, valid_in = long(M - 1) * ldx + K;
+  const long blk_out = long(R) * (Kp / 2), total_out = long(M) * (Kp / 2);
+
+  for (int i = tid; i < 8 * R; i += blockDim.x) red[i] = 0u;
+
+  RawChunk<TIn> raw[C];
+  int b = blockIdx.x;
+  {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + b * blk_in, (valid_in - b * blk_in) * ES);
 #pragma unroll
-    for (int r = 0; r < C; ++r) load_chunk<TIn, VEC>(xr + (whole[r] ? cols[r] : 0), &v[8 * r]);
+    for (int r = 0; r < C; ++r) load_raw<TIn, VEC>(rs, voff[r], raw[r]);
   }
+  __syncthreads();
+
+  long prev_m = -1;
+  int it = 0;
+  for (; b < nblocks; b += gridDim.x, ++it) {
+    b = __builtin_amdgcn_readfirstlane(b);  // uniform: keeps the buffer descriptors scalar
+    const long m = (long)b * R + rloc;
+    const bool active = slot_used && m < M;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + b * blk_in, (valid_in - b * blk_in) * ES);
+
+    if (any_partial) {  // chunks that cross column K: drop the next row's elements
+      // An opaque redefinition of K keeps the (loop-invariant) masks inside this rarely taken
+      // branch instead of being hoisted into live registers for the whole loop.
+      int Kc = K;
+      asm volatile("" : "+s"(Kc));
 #pragma unroll
-  for (int r = 0; r < C; ++r) {
-    if (__builtin_expect(!whole[r], 0)) {
-      if (active) {
-        load_chunk_tail<TIn>(xr, cols[r], K, &v[8 * r]);
-      } else {
+      for (int r = 0; r < C; ++r) mask_tail<TIn>(raw[r], j * G + 8 * chunk_of<G>(lu, r), Kc);
+    }
+    {  // raw window data, in position order, for the exact recomputation below
+      uint8_t* wb = rawwin + (wave * U + unit) * (G * ES);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[8 * r + e] = 0.0f;
+      for (int r = 0; r < C; ++r) {
+        if constexpr (sizeof(TIn) == 2) {
+          reinterpret_cast<uint4*>(wb)[chunk_of<G>(lu, r)] = raw[r].w;
+        } else {
+          reinterpret_cast<uint4*>(wb)[2 * chunk_of<G>(lu, r)] = raw[r].w0;
+          reinterpret_cast<uint4*>(wb)[2 * chunk_of<G>(lu, r) + 1] = raw[r].w1;
+        }
       }
     }
-  }
-
-  rotate_window<G>(v);
-
-  float ml = 0.0f;
+    float v[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) ml = fmaxf(ml, fabsf(v[e]));
-  const float mu = unit_max<L>(ml);
-  __syncthreads();  // row_max / row_exact cleared
-  if (active && lu == 0) atomicMax(&row_max[rloc], __float_as_uint(mu));
-  __syncthreads();
+    for (int r = 0; r < C; ++r) decode_stage0<TIn>(raw[r], &v[8 * r]);
 
-  // Exact recomputation of the absmax candidates (see candidate_slack).
-  const float mrow = active ? __uint_as_float(row_max[rloc]) : 0.0f;
-  const float thr = mrow - (mrow * candidate_slack<G>() + 1e-37f);
-  uint64_t cand = __ballot(active && mrow > 0.0f && ml >= thr);
-  while (cand) {
-    const int src = __builtin_ctzll(cand);
-    cand &= cand - 1;
-    const int s_slot = wave * U + src / L;
-    const int s_rloc = s_slot / W, s_j = s_slot - s_rloc * W, s_lu = src % L;
-    const long s_m = (long)blockIdx.x * R + s_rloc;
-    const float s_thr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr), src));
-    const TIn* srow = x + s_m * ldx;
-    uint64_t elems = 0;
+    const int bn = b + gridDim.x;
+    if (bn < nblocks) {  // prefetch the next block
+      const __amdgpu_buffer_rsrc_t rn = make_rsrc(x + bn * blk_in, (valid_in - bn * blk_in) * ES);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float a = fabsf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[e]), src)));
-      elems |= uint64_t(a >= s_thr) << e;
+      for (int r = 0; r < C; ++r) load_raw<TIn, VEC>(rn, voff[r], raw[r]);
     }
-    while (elems) {
-      const int e = __builtin_ctzll(elems);
-      elems &= elems - 1;
-      const int p = 8 * chunk_of<G>(s_lu, e >> 3) + (e & 7);
-      const float ex = exact_rotated_abs<G, TIn>(srow, K, s_j, p, lane);
-      if (lane == 0) atomicMax(&row_exact[s_rloc], __float_as_uint(ex));
+
+    rotate_window<G>(v);
+
+    float cm[C];
+    float ml = 0.0f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      float c = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c = fmaxf(c, fabsf(v[8 * r + e]));
+      cm[r] = c;
+      ml = fmaxf(ml, c);
     }
-  }
-  __syncthreads();
+    const float mu = unit_max<L>(ml);
+    uint32_t* rmax = red + (it & 3) * 2 * R;
+    uint32_t* rexact = rmax + R;
+    if (active && lu == 0) atomicMax(&rmax[rloc], __float_as_uint(mu));
+    __syncthreads();
 
-  const float amax = active ? __uint_as_float(row_exact[rloc]) : 0.0f;
-  const float scale = amax / 7.0f;                    // IEEE fp32 division
-  const float inv = amax > 0.0f ? 7.0f / amax : 0.0f;
-  if (active && lu == 0 && j == 0) s[m] = scale;
-
-  uint32_t packed[C];
-#pragma unroll
-  for (int r = 0; r < C; ++r) {
-    uint32_t b[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = __float_as_uint(__builtin_fmaf(v[8 * r + e], inv, 12582920.0f));
-    const uint32_t lo = b[0] | (b[1] << 4) | (b[2] << 8) | (b[3] << 12);
-    const uint32_t hi = b[4] | (b[5] << 4) | (b[6] << 8) | (b[7] << 12);
-    packed[r] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
-  }
-
-  // Transpose the unit's packed window through LDS so each lane stores contiguous bytes.
-  constexpr int kWinBytes = G / 2, kLaneBytes = E / 2;
-  uint8_t* ub = stage + (wave * U + unit) * kWinBytes;
-#pragma unroll
-  for (int r = 0; r < C; ++r) reinterpret_cast<uint32_t*>(ub)[chunk_of<G>(lu, r)] = packed[r];
-  __syncthreads();
-  if (active) {
-    uint8_t* qrow = q + m * (long)(Kp / 2) + (long)j * kWinBytes + lu * kLaneBytes;
-    const uint8_t* src = ub + lu * kLaneBytes;
-    if constexpr (kLaneBytes == 8) {
-      *reinterpret_cast<uint2*>(qrow) = *reinterpret_cast<const uint2*>(src);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kLaneBytes / 16; ++i)
-        reinterpret_cast<uint4*>(qrow)[i] = reinterpret_cast<const uint4*>(src)[i];
+    // Scale of the previous block: its exact maxima are complete (they precede this barrier).
+    if (prev_m >= 0 && lu == 0 && j == 0)
+      s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / 7.0f;
+    {
+      uint32_t* zb = red + ((it + 2) & 3) * 2 * R;
+      for (int i = tid; i < 2 * R; i += blockDim.x) zb[i] = 0u;
     }
-    if (xrot != nullptr) {
+
+    // Codes use the fp32 maximum; they agree with the exact one except at rounding ties.
+    const float mrow = slot_used ? __uint_as_float(rmax[rloc < R ? rloc : 0]) : 0.0f;
+    const float inv = mrow > 0.0f ? 7.0f / mrow : 0.0f;
+    uint32_t packed[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      uint32_t bits[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        bits[e] = __float_as_uint(__builtin_fmaf(v[8 * r + e], inv, 12582920.0f));
+      const uint32_t lo = (bits[3] << 12) | ((bits[2] << 8) | ((bits[1] << 4) | bits[0]));
+      const uint32_t hi = (bits[7] << 12) | ((bits[6] << 8) | ((bits[5] << 4) | bits[4]));
+      packed[r] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
+    }
+    // Transpose the unit's packed window through this wave's LDS slice so every lane
+    // stores contiguous bytes (wave-local: LDS operations of one wave complete in order).
+    uint8_t* ub = stage + (wave * U + unit) * kWinBytes;
+#pragma unroll
+    for (int r = 0; r < C; ++r) reinterpret_cast<uint32_t*>(ub)[chunk_of<G>(lu, r)] = packed[r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      const __amdgpu_buffer_rsrc_t qs = make_rsrc(q + b * blk_out, total_out - b * blk_out);
+      const uint8_t* src = ub + lu * kLaneBytes;
+      if constexpr (kLaneBytes == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned,
+                               *reinterpret_cast<const uint2*>(src)), qs, qoff, 0, 0);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kLaneBytes / 16; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned,
+                                 reinterpret_cast<const uint4*>(src)[i]), qs, qoff + 16 * i, 0, 0);
+      }
+    }
+    if (xrot != nullptr && active) {
       float* rrow = xrot + m * (long)Kp + (long)j * G;
 #pragma unroll
       for (int r = 0; r < C; ++r) {
@@ -380,20 +512,62 @@ __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__
         dst[1] = make_float4(v[8 * r + 4], v[8 * r + 5], v[8 * r + 6], v[8 * r + 7]);
       }
     }
+
+    // Exact maxima: every element within the butterfly's error bound of the row's fp32
+    // maximum is recomputed exactly (see candidate_slack); usually one per row.
+    const float thr = mrow - (mrow * candidate_slack<G>() + 1e-37f);
+    const bool live = active && mrow > 0.0f;
+#pragma unroll
+    for (int r = 0; r < C; ++r) {
+      uint64_t cand = __ballot(live && cm[r] >= thr);
+      while (cand) {  // lanes whose chunk r holds a candidate
+        const int src = __builtin_ctzll(cand);
+        cand &= cand - 1;
+        const float s_thr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr), src));
+        uint32_t elems = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float a =
+              fabsf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[8 * r + e]), src)));
+          elems |= uint32_t(a >= s_thr) << e;
+        }
+        const int s_unit = src / L;
+        const int s_rloc = __builtin_amdgcn_readlane(rloc, src), s_lu = src % L;
+        const int p0 = 8 * chunk_of<G>(s_lu, r);
+        const TIn* win = reinterpret_cast<const TIn*>(rawwin + (wave * U + s_unit) * (G * ES));
+        while (elems) {
+          const int e = __builtin_ctz(elems);
+          elems &= elems - 1;
+          const float ex = exact_rotated_abs<G, TIn>(win, p0 + e, lane);
+          if (lane == 0) atomicMax(&rexact[s_rloc], __float_as_uint(ex));
+        }
+      }
+    }
+    prev_m = active ? m : -1;
   }
+  __syncthreads();
+  if (prev_m >= 0 && lu == 0 && j == 0)
+    s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / 7.0f;
 }
 
 struct RqPlan {
   int R, waves;
 };
 
-// Rows per workgroup R and waves per workgroup so that R * W windows fill whole waves.
-RqPlan plan_rows(int W, int U) {
+// Rows per workgroup R and waves per workgroup so that R * W windows fill whole waves, with
+// the workgroup's LDS (per-row reduction slots + per-wave staging) within the 160 KiB of a CU.
+constexpr size_t kMaxLds = 160 * 1024;
+
+size_t rq_shmem(int R, int waves, int U, int G, int esize) {
+  return size_t((8 * R + 3) & ~3) * 4 + size_t(waves) * U * (G / 2) + size_t(waves) * U * G * esize;
+}
+
+RqPlan plan_rows(int W, int U, int G, int esize) {
   RqPlan best{1, (W + U - 1) / U};
   double best_eff = double(W) / (best.waves * U);
   for (int R = 2; R <= 64; ++R) {
     const int waves = (R * W + U - 1) / U;
-    if (waves > 16) break;
+    if (waves > 16 || rq_shmem(R, waves, U, G, esize) > kMaxLds) break;
     const double eff = double(R * W) / (waves * U);
     if (eff > best_eff + 1e-9) {
       best = {R, waves};
@@ -403,18 +577,49 @@ RqPlan plan_rows(int W, int U) {
   return best;
 }
 
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  static int cached[64] = {0};
+  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < 64) cached[dev] = n;
+  return n;
+}
+
+template <int G, typename TIn, int VEC>
+auto kernel_ptr() { return &rht_quant_kernel<G, TIn, VEC>; }
+
 template <int G, typename TIn, int VEC>
 hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp, uint8_t* q,
                     float* s, float* xrot, hipStream_t stream) {
-  constexpr int L = Geo<G>::L, E = Geo<G>::E, U = 64 / L;
+  constexpr int L = Geo<G>::L, U = 64 / L;
   const int W = int(Kp / G);
-  const RqPlan p = plan_rows(W, U);
-  if (p.waves > 16) return hipErrorInvalidValue;
-  const dim3 grid(unsigned((M + p.R - 1) / p.R)), block(unsigned(64 * p.waves));
-  const size_t shmem = size_t((2 * p.R + 3) & ~3) * 4 + size_t(p.waves) * U * (G / 2);
-  (void)E;
-  return launch_kernel(rht_quant_kernel<G, TIn, VEC>, grid, block, shmem, stream, x, int(M),
-                       int(K), long(ldx), int(Kp), W, p.R, q, s, xrot);
+  RqPlan p = plan_rows(W, U, G, int(sizeof(TIn)));
+  // Byte offsets inside a block are 32-bit: keep R rows of stride ldx below 2 GiB.
+  while (p.R > 1 && int64_t(p.R) * ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) {
+    p.R = 1;
+    p.waves = (W + U - 1) / U;
+  }
+  if (p.waves > 16 || ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const int nblocks = int((M + p.R - 1) / p.R);
+  const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)));
+  if (shmem > kMaxLds) return hipErrorInvalidValue;
+  if (shmem > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<G, TIn, VEC>()),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
+    if (e != hipSuccess) return e;
+  }
+  auto kernel = rht_quant_kernel<G, TIn, VEC>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * p.waves, shmem) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int grid = int(std::min<int64_t>(nblocks, int64_t(device_cus()) * per_cu));
+  return launch_kernel(kernel, dim3(unsigned(grid)), dim3(unsigned(64 * p.waves)), shmem, stream,
+                       x, int(M), int(K), long(ldx), int(Kp), W, p.R, nblocks, q, s, xrot);
 }
 
 template <typename TIn, int VEC>
@@ -436,6 +641,9 @@ hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K,
                                float* xrot, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (x_dtype == 1) {
+    // Buffer range checks are per dword: if the last valid bf16 element shares a dword with
+    // the first byte past x, wide loads would drop it, so read element by element.
+    if ((((M - 1) * ldx + K) & 1) != 0) vec_bytes = 2;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     switch (vec_bytes) {
       case 16: return launch_t<uint16_t, 16>(xb, M, K, ldx, g, Kp, q, s, xrot, stream);

@@ -117,6 +117,8 @@ def test_rotate_quant_validation(lib):
     assert _rq(lib, K=0) == E.CONVROT_ERR_SHAPE
     assert _rq(lib, ldx=63) == E.CONVROT_ERR_SHAPE
     assert _rq(lib, K=65537, ldx=65537, g=1024) == E.CONVROT_ERR_UNSUPPORTED
+    assert _rq(lib, K=61441, ldx=61441, g=1024) == E.CONVROT_ERR_UNSUPPORTED
+    assert _rq(lib, dt=0, K=32769, ldx=32769, g=1024) == E.CONVROT_ERR_UNSUPPORTED
     assert _rq(lib, K=16385, ldx=16385, g=16) == E.CONVROT_ERR_UNSUPPORTED
     assert _rq(lib, K=32769, ldx=32769, g=256) == E.CONVROT_ERR_UNSUPPORTED
     assert _rq(lib, K=32769, ldx=32769, g=64) == E.CONVROT_ERR_UNSUPPORTED

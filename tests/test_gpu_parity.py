@@ -77,14 +77,15 @@ ROTATE_CASES = [
     (200, 3072, 256, "bf16"), (37, 3100, 256, "bf16"), (5, 300, 256, "bf16"),
     (33, 777, 256, "f32"), (17, 1001, 256, "bf16"),
     (48, 12288, 1024, "bf16"), (23, 3000, 1024, "bf16"), (9, 15360, 1024, "bf16"),
-    (3, 5, 16, "bf16"), (4, 70000 // 64 * 64, 1024, "bf16"),
+    (3, 5, 16, "bf16"), (4, 70000 // 64 * 64, 1024, "bf16"), (3, 61440, 1024, "bf16"),
+    (2, 32768, 1024, "f32"), (2, 32768, 256, "bf16"), (2, 16384, 16, "f32"), (2, 32768, 64, "f32"),
 ]
 
 
 @pytest.mark.parametrize("M,K,g,dtype", ROTATE_CASES)
 def test_rotate_quant_parity(cr, M, K, g, dtype):
     _announce(f"rotate_quant M={M} K={K} g={g} {dtype}")
-    if O.padded_k(K, g) > 65536:
+    if O.padded_k(K, g) > 61440:
         with pytest.raises(cr.ConvRotError):
             cr.convrot_rotate_quant_act(_to_dev(np.zeros((M, K)), dtype), g)
         return
