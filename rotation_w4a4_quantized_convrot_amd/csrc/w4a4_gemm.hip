@@ -176,6 +176,272 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Large-tile kernel: 256 (m) x 256 (n) per workgroup, four waves of 128 x 128, each a 4 x 4
+// grid of v_mfma_i32_32x32x32_i8 blocks (the 32x32x32 form has twice the int8 throughput
+// of 16x16x64 on gfx950), K step of 128 codes.  Operands stream HBM -> LDS with buffer loads
+// straight into LDS (no VGPR staging, coalesced, rows past M or N and bytes past K' read as
+// zero) through a three-stage ring, so two K steps are in flight while one is multiplied.
+// The tile grid is walked in groups that keep each XCD's tiles in a compact block.
+namespace big {
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kTM = 128, kTN = 128;            // wave tile along m (activations) and n (weights)
+constexpr int kBM = 2 * kTM, kBN = 2 * kTN;    // workgroup tile 256 x 256
+constexpr int kGM = kTM / 32, kGN = kTN / 32;  // 32-row MFMA blocks per wave: 4 x 4
+constexpr int kAStage = kBM * kBKB;            // bytes of activation codes per stage
+constexpr int kBStage = kBN * kBKB;            // bytes of weight codes per stage
+constexpr int kStage = kAStage + kBStage;
+constexpr int kDmaA = kBM / 16, kDmaB = kBN / 16;  // 1 KB (16 rows x 64 B) transfers per stage
+constexpr int kDma = kDmaA + kDmaB;                // 32: eight per wave
+constexpr uint32_t kOob = 0x80000000u;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// XOR swizzle of the four 16-byte chunks of a 64-byte LDS row: for any fixed chunk, 8 and 16
+// consecutive rows land on distinct bank groups (conflict-free ds_read_b128 phases).
+__device__ __forceinline__ int bswz(int row, int q) {
+  return row * kChunks + (q ^ (((row >> 1) ^ (row >> 3)) & 3));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long bytes) {
+  const int n = bytes <= 0 ? 0 : bytes >= 0x7FFFFFF0L ? 0x7FFFFFF0 : int(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// Transfer g of a stage moves rows 16g..16g+15 (64 bytes each): lane i fills LDS slot
+// (row i/4, chunk i%4) with the global chunk the swizzle stores there.
+__device__ __forceinline__ uint32_t transfer_offset(int g, int lane, int rowB, int kb) {
+  const int row = 16 * g + (lane >> 2);
+  const int slot = lane & 3;
+  const int q = slot ^ (((row >> 1) ^ (row >> 3)) & 3);
+  const int byte = kb + 16 * q;
+  return byte < rowB ? uint32_t(row * rowB + byte) : kOob;
+}
+
+// This wave's eight transfers of one stage (A groups wave, wave+4, ...; then B groups).
+// A and B address their LDS region from the stage base without selects, so the compiler
+// can tell the stages apart and keep the newer transfers in flight.
+__device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t ra,
+                                            __amdgpu_buffer_rsrc_t rb, int rowB, int step,
+                                            int wave, int lane) {
+  const int kb = step * kBKB;
+#pragma unroll
+  for (int i = 0; i < kDmaA / 4; ++i) {
+    const int g = wave + 4 * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st + 1024 * g), 16,
+                                             transfer_offset(g, lane, rowB, kb), 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB / 4; ++i) {
+    const int g = wave + 4 * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(st + kAStage + 1024 * g), 16,
+                                             transfer_offset(g, lane, rowB, kb), 0, 0, 0);
+  }
+}
+
+// vmcnt(n): n = this wave's transfers of the newer stage that may stay in flight.
+__device__ __forceinline__ void wait_own_stage(bool last) {
+  if (last) __builtin_amdgcn_s_waitcnt(0x0F70);
+  else __builtin_amdgcn_s_waitcnt(0x0F70 + kDma / 4);
+}
+
+// A 32-row block fragment for one K step: lane l reads row l%32, chunks 2h and 2h+1
+// (h = l/32); after unpacking, op[s] feeds MFMA substep s (32 codes per substep: chunk
+// 2h + s/2, low or high word pair).  Weights and activations use the same mapping.
+__device__ __forceinline__ void load_block(const uint4* base, int row, int h, v4i (&op)[4]) {
+  unpack(base[bswz(row, 2 * h)], op[0], op[1]);
+  unpack(base[bswz(row, 2 * h + 1)], op[2], op[3]);
+}
+
+__device__ __forceinline__ void step_mma(const uint8_t* st, int wn, int wm, int lane,
+                                         v16i (&acc)[kGN][kGM]) {
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint4* A = reinterpret_cast<const uint4*>(st);
+  const uint4* B = reinterpret_cast<const uint4*>(st + kAStage);
+  v4i w[kGN][4], x[kGM][4];
+#pragma unroll
+  for (int i = 0; i < kGN; ++i) load_block(B, wn * kTN + 32 * i + r32, h, w[i]);
+#pragma unroll
+  for (int j = 0; j < kGM; ++j) load_block(A, wm * kTM + 32 * j + r32, h, x[j]);
+#pragma unroll
+  for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+    for (int i = 0; i < kGN; ++i)
+#pragma unroll
+      for (int j = 0; j < kGM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[i][sub], x[j][sub], acc[i][j], 0, 0, 0);
+}
+
+// Dequantization epilogue of one 256 x 256 tile.  32x32 accumulator layout: lane l holds
+// column m = l % 32 of a block and, in register r, row n = 8 (r / 4) + 4 (l / 32) + r % 4.
+//   1. The tile's 256 weight scales and biases are staged in LDS, one per thread.
+//   2. Per 32-row block of m, each lane converts its 4 x 16 accumulators and writes them as
+//      bf16 into the wave's own 32 x 128 staging rows; the wave then reads the rows back and
+//      stores 16 contiguous bytes per lane, four whole 256-byte output rows per instruction.
+template <bool kDbg>
+__device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, uint8_t* st1,
+                                         uint8_t* st2, const float* __restrict__ xs,
+                                         const float* __restrict__ ws,
+                                         const uint16_t* __restrict__ bias, int M, int N,
+                                         long m0, long n0, int wave, int lane,
+                                         uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg) {
+  constexpr int kPitch = 272;  // bytes per staging row: 256 + 16 keeps rows 16-byte aligned
+  float* fw = reinterpret_cast<float*>(st2);
+  float* fb = fw + kBN;
+  const int tid = wave * 64 + lane;
+  const bool has_bias = bias != nullptr;
+  {
+    const long n = n0 + tid;
+    fw[tid] = n < N ? ws[n] : 0.f;
+    fb[tid] = (has_bias && n < N) ? __uint_as_float(uint32_t(bias[n]) << 16) : 0.f;
+  }
+  __syncthreads();
+
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r32 = lane & 31, h = lane >> 5;
+  uint8_t* stage = (wave < 2 ? st0 : st1) + (wave & 1) * (32 * kPitch);
+  const bool vec16 = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+#pragma unroll
+  for (int j = 0; j < kGM; ++j) {
+    const long mrow = m0 + wm * kTM + 32 * j;  // first output row of this block
+    const float sxm = mrow + r32 < M ? xs[mrow + r32] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kGN; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * i + 8 * g + 4 * h;  // column within the wave's 128
+        const float4 w4 = *reinterpret_cast<const float4*>(fw + wn * kTN + c);
+        const float4 b4 = *reinterpret_cast<const float4*>(fb + wn * kTN + c);
+        const float wv[4] = {w4.x, w4.y, w4.z, w4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+        uint32_t o[4];
+        int32_t t[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          t[r] = acc[i][j][4 * g + r] >> 8;  // exact: products are multiples of 256
+          float z = __fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]);
+          if (has_bias) z = __fadd_rn(z, bv[r]);
+          o[r] = f32_to_bf16_rne(z);
+        }
+        if (kDbg && mrow + r32 < M) {  // raw integer sums, for verification only
+          const long n = n0 + wn * kTN + c;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) acc_dbg[(mrow + r32) * (long)N + n + r] = t[r];
+        }
+        *reinterpret_cast<uint2*>(stage + r32 * kPitch + 2 * c) =
+            make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+      }
+    }
+    // Same wave, in-order LDS: the rows written above are complete for the reads below.
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int row = 4 * t + (lane >> 4), c16 = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kPitch + 16 * c16);
+      const long m = mrow + row, n = n0 + wn * kTN + 8 * c16;
+      if (m < M) {
+        uint16_t* yp = y + m * (long)N + n;
+        if (vec16) {
+          if (n < N) *reinterpret_cast<uint4*>(yp) = v;
+        } else {
+          const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (n + q < N) yp[q] = uint16_t(e[q >> 1] >> (16 * (q & 1)));
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// kDbg: also store the raw integer sums (a separate instantiation keeps the production
+// kernel's register allocation free of the extra live values).
+template <bool kDbg>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                          const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+                          const uint16_t* __restrict__ bias, int M, int N, int Kp,
+                          int tiles_m, int tiles_n, uint16_t* __restrict__ y,
+                          int32_t* __restrict__ acc_dbg) {
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage], st1[kStage], st2[kStage];
+
+  // XCD-grouped tile order: blocks are dealt to the 8 XCDs round robin; give each XCD a
+  // contiguous range of tiles, walked four tile-rows at a time.
+  const int T = tiles_m * tiles_n;
+  const int per_xcd = (T + 7) / 8;
+  const int lin = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (lin >= T) return;
+  const int GH = 4;
+  const int group = lin / (GH * tiles_n), within = lin - group * GH * tiles_n;
+  const int rows_in_group = min(GH, tiles_m - group * GH);
+  // The divisions above run on the vector ALU; pin the results to scalar registers so the
+  // buffer resources built from them stay scalar (no per-load waterfall loop).
+  const int tm = __builtin_amdgcn_readfirstlane(group * GH + within % rows_in_group);
+  const int tn = __builtin_amdgcn_readfirstlane(within / rows_in_group);
+  const long m0 = (long)tm * kBM, n0 = (long)tn * kBN;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Uniform wave index, made opaque to alias analysis: were its range [0, 4) visible, the
+  // compiler could prove a read of a stage disjoint from the first transfer it recorded into
+  // that stage and then wait for every transfer in flight instead of that stage's.
+  int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  asm volatile("" : "+s"(wave));
+  const int wn = wave & 1, wm = wave >> 1;
+  const int rowB = Kp / 2;
+  const int nsteps = (rowB + kBKB - 1) / kBKB;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(xq + m0 * rowB, (long(M) - m0) * rowB);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(wq + n0 * rowB, (long(N) - n0) * rowB);
+
+  v16i acc[kGN][kGM];
+#pragma unroll
+  for (int i = 0; i < kGN; ++i)
+#pragma unroll
+    for (int j = 0; j < kGM; ++j) acc[i][j] = v16i{};
+
+  issue_stage(st0, ra, rb, rowB, 0, wave, lane);
+  issue_stage(st1, ra, rb, rowB, 1, wave, lane);  // reads zeros if nsteps == 1
+
+  // K loop, unrolled by the three stages so every LDS buffer is named statically (which
+  // lets the compiler keep the newer transfers in flight).  Ordering: each wave waits for
+  // its own transfers of the current stage (vmcnt), then a plain s_barrier makes every
+  // wave's transfers visible and guarantees the stage refilled next was fully read; a
+  // fenced __syncthreads would also drain the transfers still in flight.
+#define CONVROT_STEP(K, CUR, NXT, LAST)                                             \
+  wait_own_stage(LAST);                                                             \
+  __builtin_amdgcn_s_barrier();                                                     \
+  issue_stage(NXT, ra, rb, rowB, (K) + 2, wave, lane);                              \
+  step_mma(CUR, wn, wm, lane, acc);
+  // Steady state, free of branches: every step has a newer stage in flight.
+  int k = 0;
+  for (; k + 3 < nsteps; k += 3) {
+    CONVROT_STEP(k, st0, st2, false)
+    CONVROT_STEP(k + 1, st1, st0, false)
+    CONVROT_STEP(k + 2, st2, st1, false)
+  }
+  // One to three steps remain.  Transfers for stages past the end read zeros (their offsets
+  // are out of range) into a stage no later step reads.
+  CONVROT_STEP(k, st0, st2, k + 1 >= nsteps)
+  if (k + 1 < nsteps) {
+    CONVROT_STEP(k + 1, st1, st0, k + 2 >= nsteps)
+    if (k + 2 < nsteps) {
+      CONVROT_STEP(k + 2, st2, st1, true)
+    }
+  }
+#undef CONVROT_STEP
+
+  // Epilogue, staged through LDS so that global stores are whole rows.  The last steps may
+  // have issued zero-filling transfers after their final wait: drain them before the stage
+  // buffers are reused.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_barrier();
+  epilogue<kDbg>(acc, st0, st1, st2, xs, ws, bias, M, N, m0, n0, wave, lane, y, acc_dbg);
+}
+
+}  // namespace big
+
 }  // namespace
 
 hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq,
@@ -183,6 +449,17 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, int vec_bytes,
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  // The large tile needs 16-byte packed rows and enough work to fill the chip.
+  if ((Kp / 2) % 16 == 0 && M * N >= (int64_t(1) << 21) && M >= big::kBM / 2) {
+    const int tiles_m = int((M + big::kBM - 1) / big::kBM), tiles_n = int((N + big::kBN - 1) / big::kBN);
+    const int T = tiles_m * tiles_n;
+    const dim3 grid(unsigned(8 * ((T + 7) / 8))), block(256);
+    if (acc_dbg != nullptr)
+      return launch_kernel(big::w4a4_gemm_big_kernel<true>, grid, block, 0, stream, xq, xs, wq,
+                           ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
+    return launch_kernel(big::w4a4_gemm_big_kernel<false>, grid, block, 0, stream, xq, xs, wq, ws,
+                         bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
+  }
   const dim3 grid(unsigned((M + kBM - 1) / kBM), unsigned((N + kBN - 1) / kBN));
   const dim3 block(256);
   if (vec_bytes == 16)

@@ -171,6 +171,9 @@ GEMM_CASES = [
     # M, N, Kp, bias
     (1, 1, 16, False), (17, 5, 48, True), (128, 128, 128, False), (200, 136, 1024, True),
     (129, 130, 256, True), (300, 257, 3072, False), (64, 256, 3328, True), (33, 96, 12288, False),
+    # large-tile kernel (M N >= 2^21): ragged M and N, several tiles, K tails
+    (600, 3500, 512, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
+    (300, 7000, 3328, False),
 ]
 
 
@@ -191,10 +194,13 @@ def test_gemm_parity_full_range_codes(cr, M, N, Kp, with_bias):
     bias = None if b is None else dev(b, torch.float32).to(torch.bfloat16)
     y, acc = cr.convrot_w4a4_gemm(xq, dev(sx, torch.float32), wq, dev(sw, torch.float32), bias,
                                   want_acc=True)
+    y2 = cr.convrot_w4a4_gemm(xq, dev(sx, torch.float32), wq, dev(sw, torch.float32), bias)
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), ref["acc"])
     ybits = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(ybits, ref["out_bits"])
+    # without the integer sums requested (the production kernel instantiation)
+    assert np.array_equal(y2.view(torch.int16).cpu().numpy().view(np.uint16), ref["out_bits"])
 
 
 LINEAR_CASES = [
