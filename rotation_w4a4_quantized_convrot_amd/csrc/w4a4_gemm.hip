@@ -186,6 +186,8 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(
 namespace big {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTM = 128, kTN = 128;            // wave tile along m (activations) and n (weights)
 constexpr int kBM = 2 * kTM, kBN = 2 * kTN;    // workgroup tile 256 x 256
@@ -276,53 +278,64 @@ __device__ __forceinline__ void step_mma(const uint8_t* st, int wn, int wm, int 
 
 // Dequantization epilogue of one 256 x 256 tile.  32x32 accumulator layout: lane l holds
 // column m = l % 32 of a block and, in register r, row n = 8 (r / 4) + 4 (l / 32) + r % 4.
-//   1. The tile's 256 weight scales and biases are staged in LDS, one per thread.
-//   2. Per 32-row block of m, each lane converts its 4 x 16 accumulators and writes them as
-//      bf16 into the wave's own 32 x 128 staging rows; the wave then reads the rows back and
-//      stores 16 contiguous bytes per lane, four whole 256-byte output rows per instruction.
+//   1. The tile's 256 activation scales, weight scales and bias values (loaded into registers
+//      at kernel start, one of each per thread) are staged in LDS; each lane then keeps the
+//      factors of its 64 columns in registers.  A missing bias is -0.0, which leaves every
+//      sum unchanged in round-to-nearest-even, so the add needs no branch.
+//   2. Per 32-row block of m, each lane converts its 4 x 16 accumulators (bf16 rounding to
+//      nearest even by v_cvt_pk_bf16_f32) and writes them into the wave's own 32 x 128
+//      staging rows; the wave then reads the rows back and stores 16 contiguous bytes per
+//      lane, four whole 256-byte output rows per instruction.
 template <bool kDbg>
 __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, uint8_t* st1,
-                                         uint8_t* st2, const float* __restrict__ xs,
-                                         const float* __restrict__ ws,
-                                         const uint16_t* __restrict__ bias, int M, int N,
-                                         long m0, long n0, int wave, int lane,
-                                         uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg) {
+                                         uint8_t* st2, float xsv, float wsv, uint32_t bbits,
+                                         int M, int N, long m0, long n0, int wave, int lane,
+                                         uint16_t* __restrict__ y,
+                                         int32_t* __restrict__ acc_dbg) {
   constexpr int kPitch = 272;  // bytes per staging row: 256 + 16 keeps rows 16-byte aligned
-  float* fw = reinterpret_cast<float*>(st2);
-  float* fb = fw + kBN;
+  float* fx = reinterpret_cast<float*>(st2);
+  float* fw = fx + kBM;
+  uint16_t* fb = reinterpret_cast<uint16_t*>(fw + kBN);
   const int tid = wave * 64 + lane;
-  const bool has_bias = bias != nullptr;
-  {
-    const long n = n0 + tid;
-    fw[tid] = n < N ? ws[n] : 0.f;
-    fb[tid] = (has_bias && n < N) ? __uint_as_float(uint32_t(bias[n]) << 16) : 0.f;
-  }
+  fx[tid] = xsv;
+  fw[tid] = wsv;
+  fb[tid] = uint16_t(bbits);
   __syncthreads();
 
   const int wn = wave & 1, wm = wave >> 1;
   const int r32 = lane & 31, h = lane >> 5;
+  float4 w4[kGN][4];  // weight scales of columns 32 i + 8 g + 4 h + (0..3)
+  uint2 b4[kGN][4];   // their biases, bf16 pairs
+#pragma unroll
+  for (int i = 0; i < kGN; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = wn * kTN + 32 * i + 8 * g + 4 * h;
+      w4[i][g] = *reinterpret_cast<const float4*>(fw + c);
+      b4[i][g] = *reinterpret_cast<const uint2*>(fb + c);
+    }
   uint8_t* stage = (wave < 2 ? st0 : st1) + (wave & 1) * (32 * kPitch);
   const bool vec16 = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
 #pragma unroll
   for (int j = 0; j < kGM; ++j) {
     const long mrow = m0 + wm * kTM + 32 * j;  // first output row of this block
-    const float sxm = mrow + r32 < M ? xs[mrow + r32] : 0.f;
+    const float sxm = fx[wm * kTM + 32 * j + r32];
 #pragma unroll
     for (int i = 0; i < kGN; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = 32 * i + 8 * g + 4 * h;  // column within the wave's 128
-        const float4 w4 = *reinterpret_cast<const float4*>(fw + wn * kTN + c);
-        const float4 b4 = *reinterpret_cast<const float4*>(fb + wn * kTN + c);
-        const float wv[4] = {w4.x, w4.y, w4.z, w4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
-        uint32_t o[4];
+        const float wv[4] = {w4[i][g].x, w4[i][g].y, w4[i][g].z, w4[i][g].w};
+        const float bv[4] = {__uint_as_float(b4[i][g].x << 16),
+                             __uint_as_float(b4[i][g].x & 0xFFFF0000u),
+                             __uint_as_float(b4[i][g].y << 16),
+                             __uint_as_float(b4[i][g].y & 0xFFFF0000u)};
+        float z[4];
         int32_t t[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           t[r] = acc[i][j][4 * g + r] >> 8;  // exact: products are multiples of 256
-          float z = __fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]);
-          if (has_bias) z = __fadd_rn(z, bv[r]);
-          o[r] = f32_to_bf16_rne(z);
+          z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]), bv[r]);
         }
         if (kDbg && mrow + r32 < M) {  // raw integer sums, for verification only
           const long n = n0 + wn * kTN + c;
@@ -330,27 +343,31 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
           for (int r = 0; r < 4; ++r)
             if (n + r < N) acc_dbg[(mrow + r32) * (long)N + n + r] = t[r];
         }
+        const bf16x2 lo = __builtin_convertvector((f32x2){z[0], z[1]}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2){z[2], z[3]}, bf16x2);
         *reinterpret_cast<uint2*>(stage + r32 * kPitch + 2 * c) =
-            make_uint2(o[0] | (o[1] << 16), o[2] | (o[3] << 16));
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
     }
     // Same wave, in-order LDS: the rows written above are complete for the reads below.
     __builtin_amdgcn_wave_barrier();
+    const int c16 = lane & 15;
+    const long n = n0 + wn * kTN + 8 * c16;
+    if (vec16) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int row = 4 * t + (lane >> 4), c16 = lane & 15;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kPitch + 16 * c16);
-      const long m = mrow + row, n = n0 + wn * kTN + 8 * c16;
-      if (m < M) {
-        uint16_t* yp = y + m * (long)N + n;
-        if (vec16) {
-          if (n < N) *reinterpret_cast<uint4*>(yp) = v;
-        } else {
-          const uint32_t e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int row = 4 * t + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kPitch + 16 * c16);
+        if (mrow + row < M && n < N)
+          *reinterpret_cast<uint4*>(y + (mrow + row) * (long)N + n) = v;
+      }
+    } else {
+      for (int t = 0; t < 8; ++t) {
+        const int row = 4 * t + (lane >> 4);
+        const uint16_t* sv = reinterpret_cast<const uint16_t*>(stage + row * kPitch + 16 * c16);
+        if (mrow + row < M)
           for (int q = 0; q < 8; ++q)
-            if (n + q < N) yp[q] = uint16_t(e[q >> 1] >> (16 * (q & 1)));
-        }
+            if (n + q < N) y[(mrow + row) * (long)N + n + q] = sv[q];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -392,6 +409,16 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
   const int wn = wave & 1, wm = wave >> 1;
   const int rowB = Kp / 2;
   const int nsteps = (rowB + kBKB - 1) / kBKB;
+  // Epilogue factors, loaded now so their latency hides behind the K loop.
+  float xsv, wsv;
+  uint32_t bbits;  // bf16 bits of the bias; -0.0 (0x8000) when there is none
+  {
+    const int tid = wave * 64 + lane;
+    const long mx = m0 + tid, nx = n0 + tid;
+    xsv = mx < M ? xs[mx] : 0.f;
+    wsv = nx < N ? ws[nx] : 0.f;
+    bbits = (bias != nullptr && nx < N) ? uint32_t(bias[nx]) : 0x8000u;
+  }
   const __amdgpu_buffer_rsrc_t ra = rsrc(xq + m0 * rowB, (long(M) - m0) * rowB);
   const __amdgpu_buffer_rsrc_t rb = rsrc(wq + n0 * rowB, (long(N) - n0) * rowB);
 
@@ -437,7 +464,7 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
   // buffers are reused.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __builtin_amdgcn_s_barrier();
-  epilogue<kDbg>(acc, st0, st1, st2, xs, ws, bias, M, N, m0, n0, wave, lane, y, acc_dbg);
+  epilogue<kDbg>(acc, st0, st1, st2, xsv, wsv, bbits, M, N, m0, n0, wave, lane, y, acc_dbg);
 }
 
 }  // namespace big
