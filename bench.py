@@ -33,8 +33,8 @@ MALL_BYTES = 256 << 20          # Infinity Cache; rotate inputs through > 2x thi
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="attn_proj")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")

@@ -198,6 +198,7 @@ constexpr int kStage = kAStage + kBStage;
 constexpr int kDmaA = kBM / 16, kDmaB = kBN / 16;  // 1 KB (16 rows x 64 B) transfers per stage
 constexpr int kDma = kDmaA + kDmaB;                // 32: eight per wave
 constexpr uint32_t kOob = 0x80000000u;
+constexpr int kStages = 4;                         // LDS ring depth
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -243,37 +244,78 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t 
   }
 }
 
-// vmcnt(n): n = this wave's transfers of the newer stage that may stay in flight.
-__device__ __forceinline__ void wait_own_stage(bool last) {
-  if (last) __builtin_amdgcn_s_waitcnt(0x0F70);
-  else __builtin_amdgcn_s_waitcnt(0x0F70 + kDma / 4);
+// Wait for this wave's transfers of the oldest stage in flight but one... see the K loop:
+// the kStages - 2 newest stages (eight transfers each) may stay in flight.  vmcnt(n) is 0x0F70 + n for n < 16 and
+// sets bits 15:14 to n >> 4 above that.
+__device__ __forceinline__ void wait_own_stage() {
+  constexpr int n = (kDma / 4) * (kStages - 2);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
-// A 32-row block fragment for one K step: lane l reads row l%32, chunks 2h and 2h+1
-// (h = l/32); after unpacking, op[s] feeds MFMA substep s (32 codes per substep: chunk
-// 2h + s/2, low or high word pair).  Weights and activations use the same mapping.
-__device__ __forceinline__ void load_block(const uint4* base, int row, int h, v4i (&op)[4]) {
-  unpack(base[bswz(row, 2 * h)], op[0], op[1]);
-  unpack(base[bswz(row, 2 * h + 1)], op[2], op[3]);
-}
+// Packed fragments of one K step, as read from LDS.  For a 32-row block, lane l reads row
+// l % 32, chunks 2h and 2h + 1 (h = l / 32).  Weights and activations use the same mapping.
+struct Frags {
+  uint4 w[kGN][2], x[kGM][2];
+};
 
-__device__ __forceinline__ void step_mma(const uint8_t* st, int wn, int wm, int lane,
-                                         v16i (&acc)[kGN][kGM]) {
+__device__ __forceinline__ void read_frags(const uint8_t* st, int wn, int wm, int lane,
+                                           Frags& f) {
   const int r32 = lane & 31, h = lane >> 5;
   const uint4* A = reinterpret_cast<const uint4*>(st);
   const uint4* B = reinterpret_cast<const uint4*>(st + kAStage);
-  v4i w[kGN][4], x[kGM][4];
 #pragma unroll
-  for (int i = 0; i < kGN; ++i) load_block(B, wn * kTN + 32 * i + r32, h, w[i]);
+  for (int i = 0; i < kGN; ++i) {
+    const int row = wn * kTN + 32 * i + r32;
+    f.w[i][0] = B[bswz(row, 2 * h)];
+    f.w[i][1] = B[bswz(row, 2 * h + 1)];
+  }
 #pragma unroll
-  for (int j = 0; j < kGM; ++j) load_block(A, wm * kTM + 32 * j + r32, h, x[j]);
+  for (int j = 0; j < kGM; ++j) {
+    const int row = wm * kTM + 32 * j + r32;
+    f.x[j][0] = A[bswz(row, 2 * h)];
+    f.x[j][1] = A[bswz(row, 2 * h + 1)];
+  }
+}
+
+// MFMA operand of substep s (32 codes): dwords 0-1 (s even) or 2-3 (s odd) of chunk s / 2,
+// each dword unpacked into its even and its odd codes.
+__device__ __forceinline__ v4i unpack_sub(const uint4 (&c)[2], int s) {
+  const uint32_t m = 0xF0F0F0F0u;
+  const uint4 v = c[s >> 1];
+  const uint32_t a = (s & 1) ? v.z : v.x, b = (s & 1) ? v.w : v.y;
+  return v4i{int((a << 4) & m), int(a & m), int((b << 4) & m), int(b & m)};
+}
+
+// The unpacking of substep s + 1 is interleaved with the matrix instructions of substep s:
+// one 32-cycle MFMA leaves room for three vector instructions, so the matrix pipe is not
+// left idle while operands are prepared (sched_group_barrier masks: 8 = MFMA, 2 = VALU).
+__device__ __forceinline__ void mma_frags(const Frags& f, v16i (&acc)[kGN][kGM]) {
+  v4i w[2][kGN], x[2][kGM];
 #pragma unroll
-  for (int sub = 0; sub < 4; ++sub)
+  for (int i = 0; i < kGN; ++i) w[0][i] = unpack_sub(f.w[i], 0);
+#pragma unroll
+  for (int j = 0; j < kGM; ++j) x[0][j] = unpack_sub(f.x[j], 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = s & 1;
+    if (s < 3) {
+#pragma unroll
+      for (int i = 0; i < kGN; ++i) w[c ^ 1][i] = unpack_sub(f.w[i], s + 1);
+#pragma unroll
+      for (int j = 0; j < kGM; ++j) x[c ^ 1][j] = unpack_sub(f.x[j], s + 1);
+    }
 #pragma unroll
     for (int i = 0; i < kGN; ++i)
 #pragma unroll
       for (int j = 0; j < kGM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[i][sub], x[j][sub], acc[i][j], 0, 0, 0);
+        acc[i][j] =
+            __builtin_amdgcn_mfma_i32_32x32x32_i8(w[c][i], x[c][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kGN * kGM; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  }
 }
 
 // Dequantization epilogue of one 256 x 256 tile.  32x32 accumulator layout: lane l holds
@@ -383,7 +425,8 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
                           const uint16_t* __restrict__ bias, int M, int N, int Kp,
                           int tiles_m, int tiles_n, uint16_t* __restrict__ y,
                           int32_t* __restrict__ acc_dbg) {
-  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage], st1[kStage], st2[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage], st1[kStage], st2[kStage],
+      st3[kStage];
 
   // XCD-grouped tile order: blocks are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous range of tiles, walked four tile-rows at a time.
@@ -428,39 +471,52 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
 #pragma unroll
     for (int j = 0; j < kGM; ++j) acc[i][j] = v16i{};
 
+  // The ring: stage k of the K loop lives in buffer k % 4, and the fragments of stage k + 1
+  // are read from LDS while the matrix cores work on stage k.  Transfers are issued for
+  // every step, also past the end (their offsets are then out of range and they write
+  // zeros that no step uses), so that every wait has the same form.  Ordering at the top of
+  // step k: each wave waits for its own transfers of stage k + 1 (vmcnt) and for its reads
+  // of stage k (lgkmcnt); a plain s_barrier then makes every wave's transfers visible and
+  // guarantees that no wave still reads buffer k % 4, which is refilled with stage k + 4.
+  // (A fenced __syncthreads would also drain the transfers still in flight.)  The loop is
+  // unrolled by four so every buffer is named statically, which lets the compiler keep the
+  // newer transfers in flight.
+  Frags fa, fb;
   issue_stage(st0, ra, rb, rowB, 0, wave, lane);
-  issue_stage(st1, ra, rb, rowB, 1, wave, lane);  // reads zeros if nsteps == 1
-
-  // K loop, unrolled by the three stages so every LDS buffer is named statically (which
-  // lets the compiler keep the newer transfers in flight).  Ordering: each wave waits for
-  // its own transfers of the current stage (vmcnt), then a plain s_barrier makes every
-  // wave's transfers visible and guarantees the stage refilled next was fully read; a
-  // fenced __syncthreads would also drain the transfers still in flight.
-#define CONVROT_STEP(K, CUR, NXT, LAST)                                             \
-  wait_own_stage(LAST);                                                             \
+  issue_stage(st1, ra, rb, rowB, 1, wave, lane);
+  issue_stage(st2, ra, rb, rowB, 2, wave, lane);
+  wait_own_stage();
+  __builtin_amdgcn_s_barrier();
+  issue_stage(st3, ra, rb, rowB, 3, wave, lane);
+  read_frags(st0, wn, wm, lane, fa);
+#define CONVROT_STEP(K, NEXT, REFILL, CUR, NXT)                                     \
+  wait_own_stage();                                                                 \
+  __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                              \
   __builtin_amdgcn_s_barrier();                                                     \
-  issue_stage(NXT, ra, rb, rowB, (K) + 2, wave, lane);                              \
-  step_mma(CUR, wn, wm, lane, acc);
-  // Steady state, free of branches: every step has a newer stage in flight.
+  issue_stage(REFILL, ra, rb, rowB, (K) + 4, wave, lane);                           \
+  read_frags(NEXT, wn, wm, lane, NXT);                                              \
+  __builtin_amdgcn_sched_barrier(0); /* reads first: they have a whole step to land */ \
+  mma_frags(CUR, acc);
   int k = 0;
-  for (; k + 3 < nsteps; k += 3) {
-    CONVROT_STEP(k, st0, st2, false)
-    CONVROT_STEP(k + 1, st1, st0, false)
-    CONVROT_STEP(k + 2, st2, st1, false)
+  for (; k + 4 <= nsteps; k += 4) {
+    CONVROT_STEP(k, st1, st0, fa, fb)
+    CONVROT_STEP(k + 1, st2, st1, fb, fa)
+    CONVROT_STEP(k + 2, st3, st2, fa, fb)
+    CONVROT_STEP(k + 3, st0, st3, fb, fa)
   }
-  // One to three steps remain.  Transfers for stages past the end read zeros (their offsets
-  // are out of range) into a stage no later step reads.
-  CONVROT_STEP(k, st0, st2, k + 1 >= nsteps)
-  if (k + 1 < nsteps) {
-    CONVROT_STEP(k + 1, st1, st0, k + 2 >= nsteps)
-    if (k + 2 < nsteps) {
-      CONVROT_STEP(k + 2, st2, st1, true)
+  if (k < nsteps) {
+    CONVROT_STEP(k, st1, st0, fa, fb)
+    if (k + 1 < nsteps) {
+      CONVROT_STEP(k + 1, st2, st1, fb, fa)
+      if (k + 2 < nsteps) {
+        CONVROT_STEP(k + 2, st3, st2, fa, fb)
+      }
     }
   }
 #undef CONVROT_STEP
 
-  // Epilogue, staged through LDS so that global stores are whole rows.  The last steps may
-  // have issued zero-filling transfers after their final wait: drain them before the stage
+  // Epilogue, staged through LDS so that global stores are whole rows.  The last steps
+  // issued zero-filling transfers after their final wait: drain them before the stage
   // buffers are reused.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __builtin_amdgcn_s_barrier();
