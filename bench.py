@@ -5,12 +5,14 @@ One step = the whole hot path on one batch: rotate + quantize the activations
 (convrot_rotate_quant_act) and the W4A4 GEMM with the fused dequant epilogue
 (convrot_w4a4_gemm), i.e. the two kernels convrot_w4a4_linear enqueues, launched through
 the C ABI.  The weights are rotated and quantized once, before timing (offline path).
+Activations rotate through more than twice the 256 MB Infinity Cache, so they come from HBM.
 
-Prints ONE JSON line.  `value` is the full-layer throughput 2 M N K' / step time.  The
-`roofline` object is for the dominant kernel (the GEMM, int8 matrix cores); the
-rotate+quantize kernel's HBM roofline is reported alongside.  Per-kernel durations come
-from HIP events recorded on the launch stream inside the timed region.  The CPU oracle is
-timed on a bounded sample of the same workload (`cpu_baseline`).
+Prints ONE JSON line.  `value` is the full-layer throughput 2 M N K' / step time over the
+timed steps.  The `roofline` object is for the dominant kernel (the GEMM, int8 matrix
+cores); the rotate+quantize kernel's HBM roofline is reported alongside.  Each kernel's
+launch duration comes from HIP events on the launch stream around batches of back-to-back
+launches of that kernel.  The CPU oracle is timed over whole passes of the same layer
+(`cpu_baseline`).
 """
 from __future__ import annotations
 
@@ -37,7 +39,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="attn_proj")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = auto)")
+    p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = all)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="time the oracle over whole passes until this many seconds")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for HBM counter scaling)")
     return p.parse_args()
@@ -115,32 +119,49 @@ def gpu_bench(args, wl):
 
     hip = Hip()
     K_steps = args.steps
-    ev = [[hip.event() for _ in range(3)] for _ in range(K_steps)]
+    # Timed region: K whole steps back to back, bracketed by a synchronisation on each side
+    # (events only at the two ends: an event between kernels costs several microseconds).
+    e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    hip.record(e0, stream)
     for i in range(K_steps):
-        e = ev[i]
-        hip.record(e[0], stream)
-        rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream)
-        hip.record(e[1], stream)
-        gemm(xq_p, xs_p, wq_p, ws_p, b_ptr, M, N, Kp, y_ptrs[i % n_y], None, stream)
-        hip.record(e[2], stream)
+        step(i)
+    hip.record(e1, stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    rq_ms = np.array([hip.ms(e[0], e[1]) for e in ev])
-    gemm_ms = np.array([hip.ms(e[1], e[2]) for e in ev])
-    for e in ev:
-        for x in e:
-            hip.lib.hipEventDestroy(x)
+    step_ms_events = hip.ms(e0, e1) / K_steps
+
+    # Launch duration of each kernel: batches of back-to-back launches of that kernel alone,
+    # on the same inputs (the activations still rotate through the HBM-sized buffer set),
+    # with events around each batch on the launch stream.
+    def batches(fn, n_batches=5, per_batch=max(20, K_steps // 5)):
+        out = []
+        for bi in range(n_batches):
+            hip.record(e0, stream)
+            for i in range(per_batch):
+                fn(bi * per_batch + i)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            out.append(hip.ms(e0, e1) / per_batch)
+        return np.array(out)
+
+    rq_ms = batches(lambda i: rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream))
+    gemm_ms = batches(lambda i: gemm(xq_p, xs_p, wq_p, ws_p, b_ptr, M, N, Kp, y_ptrs[i % n_y],
+                                     None, stream))
+    for x in (e0, e1):
+        hip.lib.hipEventDestroy(x)
 
     copy = None
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.uint8, device=dev)   # 256 MiB
+        # a plain elementwise kernel that reads 256 MiB and writes 256 MiB, for scaling the
+        # HBM byte counters (see rotation_w4a4_quantized_convrot_amd/profiling.py)
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        copy = {"bytes_each_way": src.numel(), "launches": 3}
+        copy = {"bytes_each_way": src.numel() * 4, "launches": 3}
 
     ms_step = (t1 - t0) * 1e3 / K_steps
     ops = 2.0 * M * N * Kp
@@ -152,7 +173,7 @@ def gpu_bench(args, wl):
     # GEMM algorithmic bytes: packed operands once, scales, bias, bf16 output
     gemm_bytes = M * Kp // 2 + N * Kp // 2 + 4 * (M + N) + (2 * N if bias is not None else 0) + 2 * M * N
     return {
-        "ms_per_step": ms_step,
+        "ms_per_step": ms_step, "ms_per_step_events": step_ms_events,
         "value": ops / (ms_step * 1e-3) / 1e12,
         "rq_us": rq_us, "rq_us_median": float(np.median(rq_ms) * 1e3), "rq_bytes": rq_bytes,
         "rq_gbps": rq_gbps, "gemm_us": gemm_us, "gemm_us_median": float(np.median(gemm_ms) * 1e3),
@@ -162,8 +183,8 @@ def gpu_bench(args, wl):
 
 
 def cpu_baseline(args, wl):
-    """The oracle, as it stands, on a bounded row sample of the same workload."""
-    import numpy as np
+    """The oracle, as it stands, timed on the host: whole passes of the same layer (all rows,
+    rotate + quantize, integer GEMM, dequantization) until about --cpu-seconds have passed."""
     import threadpoolctl
 
     import workloads as wkmod
@@ -173,17 +194,21 @@ def cpu_baseline(args, wl):
     w = wkmod.weights(wl)
     b = wkmod.bias(wl)
     refw = O.quantize_weight(w, wl.g)               # offline path, not timed
-    rows = args.cpu_rows or min(wl.M, 1024)
+    rows = args.cpu_rows or wl.M
     xs = x[:rows]
-    t0 = time.perf_counter()
-    r = O.rotate_quantize(xs, wl.g)
-    O.w4a4_linear_from_codes(r["codes"], r["scale"], refw["codes"], refw["scale"], b)
-    dt = time.perf_counter() - t0
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        r = O.rotate_quantize(xs, wl.g)
+        O.w4a4_linear_from_codes(r["codes"], r["scale"], refw["codes"], refw["scale"], b)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= args.cpu_seconds or passes >= 100:
+            break
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    ops = 2.0 * rows * wl.N * wl.Kp
+    ops = 2.0 * rows * wl.N * wl.Kp * passes
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows} of {wl.M} rows, all {wl.N} outputs: rotate+quantize + GEMM + "
-                      f"dequant ({dt:.1f} s)",
+            "sample": f"{passes} passes of the layer on {rows} of {wl.M} rows, all {wl.N} "
+                      f"outputs (rotate+quantize, int GEMM, dequant; {dt:.1f} s)",
             "seconds": dt}
 
 
@@ -199,12 +224,22 @@ def main():
         raise SystemExit("the benchmark needs a workload with a weight (N)")
     r = gpu_bench(args, wl)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl)
+    from rotation_w4a4_quantized_convrot_amd import profiling
+    big = (wl.Kp // 2) % 16 == 0 and wl.M * wl.N >= (1 << 21) and wl.M >= 128
+    gemm_kernel = "w4a4_gemm_big_kernel" if big else "w4a4_gemm_kernel"
+    tg = profiling.read_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.txt"), gemm_kernel) \
+        if big else None
+    tq = profiling.read_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.txt"),
+                                "rht_quant_kernel") if wl.g == 256 else None
     roof = {"bound": "mfma", "achieved": r["gemm_tops"], "peak": INT8_PEAK_TOPS,
-            "unit": "TFLOP/s", "frac": r["gemm_tops"] / INT8_PEAK_TOPS, "traffic": None,
-            "kernel": "w4a4_gemm_kernel", "launch_us": r["gemm_us"],
-            "algorithmic_ops_per_launch": r["gemm_ops"]}
+            "unit": "TFLOP/s", "frac": r["gemm_tops"] / INT8_PEAK_TOPS,
+            "traffic": None if tg is None else tg["fetch_bytes"] + tg["write_bytes"],
+            "kernel": gemm_kernel, "launch_us": r["gemm_us"],
+            "algorithmic_ops_per_launch": r["gemm_ops"],
+            "algorithmic_bytes_per_launch": r["gemm_bytes"]}
     roof_rq = {"bound": "hbm", "achieved": r["rq_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-               "frac": r["rq_gbps"] / HBM_PEAK_GBPS, "traffic": None,
+               "frac": r["rq_gbps"] / HBM_PEAK_GBPS,
+               "traffic": None if tq is None else tq["fetch_bytes"] + tq["write_bytes"],
                "kernel": "rht_quant_kernel", "launch_us": r["rq_us"],
                "algorithmic_bytes_per_launch": r["rq_bytes"]}
     out = {

@@ -1,0 +1,54 @@
+"""Host-side checks of the rocprofv3 summary helpers (no GPU, synthetic CSV files)."""
+import csv
+import os
+
+import pytest
+
+from rotation_w4a4_quantized_convrot_amd import profiling as P
+
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+          "Counter_Value"]
+
+
+def _write(d, counter, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "bench_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, grid, val) in enumerate(rows):
+            w.writerow({"Correlation_Id": i, "Dispatch_Id": i, "Kernel_Name": name,
+                        "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": val})
+
+
+GEMM = "void convrot::(anonymous namespace)::big::w4a4_gemm_big_kernel<false>(...)"
+CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<...>>"
+
+
+def test_traffic_scaling_and_staleness(tmp_path):
+    # the calibration copy reads half of its 256 MiB according to the counter: scale 2
+    _write(tmp_path / "f", "FETCH_SIZE", [(GEMM, 55296, 999.0), (GEMM, 55296, 100.0),
+                                          (GEMM, 55296, 100.0), (CAL, 262144, 131072.0),
+                                          (CAL, 1024, 5.0)])
+    _write(tmp_path / "w", "WRITE_SIZE", [(GEMM, 55296, 50.0), (GEMM, 55296, 50.0),
+                                          (CAL, 262144, 262144.0)])
+    t = P.traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+    g = t["w4a4_gemm_big_kernel"]
+    assert g["fetch_scale"] == pytest.approx(2.0) and g["write_scale"] == pytest.approx(1.0)
+    assert g["fetch_bytes"] == pytest.approx(100.0 * 1024 * 2)    # first (cold) dispatch left out
+    assert g["write_bytes"] == pytest.approx(50.0 * 1024)
+    out = tmp_path / "traffic.txt"
+    P.write_traffic(str(out), t, "cmd")
+    r = P.read_traffic(str(out), "w4a4_gemm_big_kernel")
+    assert r == {"fetch_bytes": pytest.approx(204800.0), "write_bytes": pytest.approx(51200.0)}
+    # a different source hash means the kernel changed since: no traffic figure
+    text = out.read_text().replace(g["source_sha256"], "0" * 64)
+    out.write_text(text)
+    assert P.read_traffic(str(out), "w4a4_gemm_big_kernel") is None
+    assert P.read_traffic(str(tmp_path / "missing.txt"), "w4a4_gemm_big_kernel") is None
+
+
+def test_calibration_required(tmp_path):
+    _write(tmp_path / "f", "FETCH_SIZE", [(GEMM, 55296, 1.0)])
+    _write(tmp_path / "w", "WRITE_SIZE", [(GEMM, 55296, 1.0)])
+    with pytest.raises(ValueError):
+        P.traffic(str(tmp_path / "f"), str(tmp_path / "w"))
