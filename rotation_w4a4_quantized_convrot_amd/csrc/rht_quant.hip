@@ -40,6 +40,10 @@ template <> struct Geo<64>   { static constexpr int KD = 3, L = 2,  E = 32; };
 template <> struct Geo<256>  { static constexpr int KD = 4, L = 8,  E = 32; };
 template <> struct Geo<1024> { static constexpr int KD = 5, L = 16, E = 64; };
 
+// Cache policy of the code stores: non-temporal (streaming), bit 1 of the buffer
+// instruction's cache-policy operand on gfx950.
+constexpr int kStreamStore = 2;
+
 // DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
 constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
@@ -494,13 +498,13 @@ __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__
       if constexpr (kLaneBytes == 8) {
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned,
-                               *reinterpret_cast<const uint2*>(src)), qs, qoff, 0, 0);
+                               *reinterpret_cast<const uint2*>(src)), qs, qoff, 0, kStreamStore);
       } else {
 #pragma unroll
         for (int i = 0; i < kLaneBytes / 16; ++i)
           __builtin_amdgcn_raw_buffer_store_b128(
               __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned,
-                                 reinterpret_cast<const uint4*>(src)[i]), qs, qoff + 16 * i, 0, 0);
+                                 reinterpret_cast<const uint4*>(src)[i]), qs, qoff + 16 * i, 0, kStreamStore);
       }
     }
     if (xrot != nullptr && active) {

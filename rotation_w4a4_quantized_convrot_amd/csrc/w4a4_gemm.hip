@@ -187,6 +187,7 @@ namespace big {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTM = 128, kTN = 128;            // wave tile along m (activations) and n (weights)
@@ -400,8 +401,9 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
       for (int t = 0; t < 8; ++t) {
         const int row = 4 * t + (lane >> 4);
         const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kPitch + 16 * c16);
-        if (mrow + row < M && n < N)
-          *reinterpret_cast<uint4*>(y + (mrow + row) * (long)N + n) = v;
+        if (mrow + row < M && n < N)  // streaming store: the output is not re-read here
+          __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                      reinterpret_cast<u32x4*>(y + (mrow + row) * (long)N + n));
       }
     } else {
       for (int t = 0; t < 8; ++t) {
