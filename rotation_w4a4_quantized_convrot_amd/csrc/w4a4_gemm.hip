@@ -190,14 +190,21 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kTM = 128, kTN = 128;            // wave tile along m (activations) and n (weights)
-constexpr int kBM = 2 * kTM, kBN = 2 * kTN;    // workgroup tile 256 x 256
-constexpr int kGM = kTM / 32, kGN = kTN / 32;  // 32-row MFMA blocks per wave: 4 x 4
+#ifndef CONVROT_GEMM_WAVES
+#define CONVROT_GEMM_WAVES 8
+#endif
+constexpr int kWaves = CONVROT_GEMM_WAVES;     // 4: one wave per SIMD; 8: two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 256, kBN = 256;            // workgroup tile along m (activations) and n
+constexpr int kWavesN = 2, kWavesM = kWaves / kWavesN;
+constexpr int kTM = kBM / kWavesM, kTN = kBN / kWavesN;  // wave tile
+constexpr int kGM = kTM / 32, kGN = kTN / 32;  // 32-row MFMA blocks per wave
 constexpr int kAStage = kBM * kBKB;            // bytes of activation codes per stage
 constexpr int kBStage = kBN * kBKB;            // bytes of weight codes per stage
 constexpr int kStage = kAStage + kBStage;
 constexpr int kDmaA = kBM / 16, kDmaB = kBN / 16;  // 1 KB (16 rows x 64 B) transfers per stage
-constexpr int kDma = kDmaA + kDmaB;                // 32: eight per wave
+constexpr int kDma = kDmaA + kDmaB;                // 32 per stage
+constexpr int kDmaPerWave = kDma / kWaves;
 constexpr uint32_t kOob = 0x80000000u;
 constexpr int kStages = 4;                         // LDS ring depth
 
@@ -224,7 +231,7 @@ __device__ __forceinline__ uint32_t transfer_offset(int g, int lane, int rowB, i
   return byte < rowB ? uint32_t(row * rowB + byte) : kOob;
 }
 
-// This wave's eight transfers of one stage (A groups wave, wave+4, ...; then B groups).
+// This wave's transfers of one stage (A groups wave, wave + kWaves, ...; then B groups).
 // A and B address their LDS region from the stage base without selects, so the compiler
 // can tell the stages apart and keep the newer transfers in flight.
 __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t ra,
@@ -232,24 +239,24 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t 
                                             int wave, int lane) {
   const int kb = step * kBKB;
 #pragma unroll
-  for (int i = 0; i < kDmaA / 4; ++i) {
-    const int g = wave + 4 * i;
+  for (int i = 0; i < kDmaA / kWaves; ++i) {
+    const int g = wave + kWaves * i;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st + 1024 * g), 16,
                                              transfer_offset(g, lane, rowB, kb), 0, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < kDmaB / 4; ++i) {
-    const int g = wave + 4 * i;
+  for (int i = 0; i < kDmaB / kWaves; ++i) {
+    const int g = wave + kWaves * i;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(st + kAStage + 1024 * g), 16,
                                              transfer_offset(g, lane, rowB, kb), 0, 0, 0);
   }
 }
 
-// Wait for this wave's transfers of the oldest stage in flight but one... see the K loop:
-// the kStages - 2 newest stages (eight transfers each) may stay in flight.  vmcnt(n) is 0x0F70 + n for n < 16 and
+// Wait for this wave's transfers of the stage needed next (see the K loop): those of the
+// kStages - 2 newest stages may stay in flight.  vmcnt(n) is 0x0F70 + n for n < 16 and
 // sets bits 15:14 to n >> 4 above that.
 __device__ __forceinline__ void wait_own_stage() {
-  constexpr int n = (kDma / 4) * (kStages - 2);
+  constexpr int n = kDmaPerWave * (kStages - 2);
   __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
 }
 
@@ -288,7 +295,7 @@ __device__ __forceinline__ v4i unpack_sub(const uint4 (&c)[2], int s) {
 }
 
 // The unpacking of substep s + 1 is interleaved with the matrix instructions of substep s:
-// one 32-cycle MFMA leaves room for three vector instructions, so the matrix pipe is not
+// one 32-cycle MFMA leaves room for several vector instructions, so the matrix pipe is not
 // left idle while operands are prepared (sched_group_barrier masks: 8 = MFMA, 2 = VALU).
 __device__ __forceinline__ void mma_frags(const Frags& f, v16i (&acc)[kGN][kGM]) {
   v4i w[2][kGN], x[2][kGM];
@@ -311,10 +318,11 @@ __device__ __forceinline__ void mma_frags(const Frags& f, v16i (&acc)[kGN][kGM])
       for (int j = 0; j < kGM; ++j)
         acc[i][j] =
             __builtin_amdgcn_mfma_i32_32x32x32_i8(w[c][i], x[c][j], acc[i][j], 0, 0, 0);
+    constexpr int kValuPerMfma = (6 * (kGN + kGM) + kGN * kGM - 1) / (kGN * kGM);
 #pragma unroll
     for (int q = 0; q < kGN * kGM; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
     }
   }
 }
@@ -331,33 +339,27 @@ __device__ __forceinline__ void mma_frags(const Frags& f, v16i (&acc)[kGN][kGM])
 //      lane, four whole 256-byte output rows per instruction.
 template <bool kDbg>
 __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, uint8_t* st1,
-                                         uint8_t* st2, float xsv, float wsv, uint32_t bbits,
+                                         uint8_t* st2, uint8_t* st3, float xsv, float wsv,
+                                         uint32_t bbits,
                                          int M, int N, long m0, long n0, int wave, int lane,
                                          uint16_t* __restrict__ y,
                                          int32_t* __restrict__ acc_dbg) {
   constexpr int kPitch = 272;  // bytes per staging row: 256 + 16 keeps rows 16-byte aligned
-  float* fx = reinterpret_cast<float*>(st2);
+  float* fx = reinterpret_cast<float*>(st3);
   float* fw = fx + kBM;
   uint16_t* fb = reinterpret_cast<uint16_t*>(fw + kBN);
   const int tid = wave * 64 + lane;
-  fx[tid] = xsv;
-  fw[tid] = wsv;
-  fb[tid] = uint16_t(bbits);
+  if (tid < kBM) {  // kBM == kBN
+    fx[tid] = xsv;
+    fw[tid] = wsv;
+    fb[tid] = uint16_t(bbits);
+  }
   __syncthreads();
 
   const int wn = wave & 1, wm = wave >> 1;
   const int r32 = lane & 31, h = lane >> 5;
-  float4 w4[kGN][4];  // weight scales of columns 32 i + 8 g + 4 h + (0..3)
-  uint2 b4[kGN][4];   // their biases, bf16 pairs
-#pragma unroll
-  for (int i = 0; i < kGN; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int c = wn * kTN + 32 * i + 8 * g + 4 * h;
-      w4[i][g] = *reinterpret_cast<const float4*>(fw + c);
-      b4[i][g] = *reinterpret_cast<const uint2*>(fb + c);
-    }
-  uint8_t* stage = (wave < 2 ? st0 : st1) + (wave & 1) * (32 * kPitch);
+  // Each wave's 32 x 128 staging rows: three per stage buffer (st3 holds the factors).
+  uint8_t* stage = (wave < 3 ? st0 : wave < 6 ? st1 : st2) + (wave % 3) * (32 * kPitch);
   const bool vec16 = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
 #pragma unroll
   for (int j = 0; j < kGM; ++j) {
@@ -368,11 +370,11 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = 32 * i + 8 * g + 4 * h;  // column within the wave's 128
-        const float wv[4] = {w4[i][g].x, w4[i][g].y, w4[i][g].z, w4[i][g].w};
-        const float bv[4] = {__uint_as_float(b4[i][g].x << 16),
-                             __uint_as_float(b4[i][g].x & 0xFFFF0000u),
-                             __uint_as_float(b4[i][g].y << 16),
-                             __uint_as_float(b4[i][g].y & 0xFFFF0000u)};
+        const float4 w4 = *reinterpret_cast<const float4*>(fw + wn * kTN + c);
+        const uint2 b4 = *reinterpret_cast<const uint2*>(fb + wn * kTN + c);
+        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+        const float bv[4] = {__uint_as_float(b4.x << 16), __uint_as_float(b4.x & 0xFFFF0000u),
+                             __uint_as_float(b4.y << 16), __uint_as_float(b4.y & 0xFFFF0000u)};
         float z[4];
         int32_t t[4];
 #pragma unroll
@@ -421,7 +423,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
 // kDbg: also store the raw integer sums (a separate instantiation keeps the production
 // kernel's register allocation free of the extra live values).
 template <bool kDbg>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
                           const uint8_t* __restrict__ wq, const float* __restrict__ ws,
                           const uint16_t* __restrict__ bias, int M, int N, int Kp,
@@ -458,11 +461,12 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
   float xsv, wsv;
   uint32_t bbits;  // bf16 bits of the bias; -0.0 (0x8000) when there is none
   {
-    const int tid = wave * 64 + lane;
+    const int tid = wave * 64 + lane;  // one row and one column of the tile per thread
     const long mx = m0 + tid, nx = n0 + tid;
-    xsv = mx < M ? xs[mx] : 0.f;
-    wsv = nx < N ? ws[nx] : 0.f;
-    bbits = (bias != nullptr && nx < N) ? uint32_t(bias[nx]) : 0x8000u;
+    const bool own = tid < kBM;
+    xsv = own && mx < M ? xs[mx] : 0.f;
+    wsv = own && nx < N ? ws[nx] : 0.f;
+    bbits = (own && bias != nullptr && nx < N) ? uint32_t(bias[nx]) : 0x8000u;
   }
   const __amdgpu_buffer_rsrc_t ra = rsrc(xq + m0 * rowB, (long(M) - m0) * rowB);
   const __amdgpu_buffer_rsrc_t rb = rsrc(wq + n0 * rowB, (long(N) - n0) * rowB);
@@ -483,6 +487,38 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
   // (A fenced __syncthreads would also drain the transfers still in flight.)  The loop is
   // unrolled by four so every buffer is named statically, which lets the compiler keep the
   // newer transfers in flight.
+#if CONVROT_GEMM_WAVES == 8
+  // Two waves per SIMD: the other wave hides the fragment reads, so they are read in the
+  // step that uses them (one fragment set keeps the wave within 256 registers).  Step k
+  // waits for stage k and refills the buffer read in step k - 1 with stage k + 3.
+  Frags f;
+  issue_stage(st0, ra, rb, rowB, 0, wave, lane);
+  issue_stage(st1, ra, rb, rowB, 1, wave, lane);
+  issue_stage(st2, ra, rb, rowB, 2, wave, lane);
+#define CONVROT_STEP(K, CUR, REFILL)                                                \
+  wait_own_stage();                                                                 \
+  __builtin_amdgcn_s_barrier();                                                     \
+  issue_stage(REFILL, ra, rb, rowB, (K) + 3, wave, lane);                           \
+  read_frags(CUR, wn, wm, lane, f);                                                 \
+  mma_frags(f, acc);
+  int k = 0;
+  for (; k + 4 <= nsteps; k += 4) {
+    CONVROT_STEP(k, st0, st3)
+    CONVROT_STEP(k + 1, st1, st0)
+    CONVROT_STEP(k + 2, st2, st1)
+    CONVROT_STEP(k + 3, st3, st2)
+  }
+  if (k < nsteps) {
+    CONVROT_STEP(k, st0, st3)
+    if (k + 1 < nsteps) {
+      CONVROT_STEP(k + 1, st1, st0)
+      if (k + 2 < nsteps) {
+        CONVROT_STEP(k + 2, st2, st1)
+      }
+    }
+  }
+#undef CONVROT_STEP
+#else
   Frags fa, fb;
   issue_stage(st0, ra, rb, rowB, 0, wave, lane);
   issue_stage(st1, ra, rb, rowB, 1, wave, lane);
@@ -516,13 +552,15 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
     }
   }
 #undef CONVROT_STEP
+#endif
 
   // Epilogue, staged through LDS so that global stores are whole rows.  The last steps
   // issued zero-filling transfers after their final wait: drain them before the stage
   // buffers are reused.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __builtin_amdgcn_s_barrier();
-  epilogue<kDbg>(acc, st0, st1, st2, xsv, wsv, bbits, M, N, m0, n0, wave, lane, y, acc_dbg);
+  epilogue<kDbg>(acc, st0, st1, st2, st3, xsv, wsv, bbits, M, N, m0, n0, wave, lane, y,
+                 acc_dbg);
 }
 
 }  // namespace big
@@ -538,7 +576,7 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
   if ((Kp / 2) % 16 == 0 && M * N >= (int64_t(1) << 21) && M >= big::kBM / 2) {
     const int tiles_m = int((M + big::kBM - 1) / big::kBM), tiles_n = int((N + big::kBN - 1) / big::kBN);
     const int T = tiles_m * tiles_n;
-    const dim3 grid(unsigned(8 * ((T + 7) / 8))), block(256);
+    const dim3 grid(unsigned(8 * ((T + 7) / 8))), block(big::kThreads);
     if (acc_dbg != nullptr)
       return launch_kernel(big::w4a4_gemm_big_kernel<true>, grid, block, 0, stream, xq, xs, wq,
                            ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
