@@ -296,6 +296,45 @@ __device__ __forceinline__ v4i unpack_sub(const uint4 (&c)[2], int s) {
   return v4i{int((a << 4) & m), int(a & m), int((b << 4) & m), int(b & m)};
 }
 
+// One chunk (substeps 2c and 2c + 1) of every block's fragment.
+struct Half {
+  uint4 w[kGN], x[kGM];
+};
+
+__device__ __forceinline__ void read_half(const uint8_t* st, int c, int wn, int wm, int lane,
+                                          Half& f) {
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint4* A = reinterpret_cast<const uint4*>(st);
+  const uint4* B = reinterpret_cast<const uint4*>(st + kAStage);
+#pragma unroll
+  for (int j = 0; j < kGM; ++j) f.x[j] = A[bswz(wm * kTM + 32 * j + r32, 2 * h + c)];
+#pragma unroll
+  for (int i = 0; i < kGN; ++i) f.w[i] = B[bswz(wn * kTN + 32 * i + r32, 2 * h + c)];
+}
+
+__device__ __forceinline__ v4i unpack_half(const uint4 v, int s) {
+  const uint32_t m = 0xF0F0F0F0u;
+  const uint32_t a = (s & 1) ? v.z : v.x, b = (s & 1) ? v.w : v.y;
+  return v4i{int((a << 4) & m), int(a & m), int((b << 4) & m), int(b & m)};
+}
+
+// The two substeps of one chunk.
+__device__ __forceinline__ void mma_half(const Half& f, v16i (&acc)[kGN][kGM]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v4i w[kGN], x[kGM];
+#pragma unroll
+    for (int i = 0; i < kGN; ++i) w[i] = unpack_half(f.w[i], s);
+#pragma unroll
+    for (int j = 0; j < kGM; ++j) x[j] = unpack_half(f.x[j], s);
+#pragma unroll
+    for (int i = 0; i < kGN; ++i)
+#pragma unroll
+      for (int j = 0; j < kGM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w[i], x[j], acc[i][j], 0, 0, 0);
+  }
+}
+
 // The unpacking of substep s + 1 is interleaved with the matrix instructions of substep s:
 // one 32-cycle MFMA leaves room for several vector instructions, so the matrix pipe is not
 // left idle while operands are prepared (sched_group_barrier masks: 8 = MFMA, 2 = VALU).
@@ -490,32 +529,42 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
   // unrolled by four so every buffer is named statically, which lets the compiler keep the
   // newer transfers in flight.
 #if CONVROT_GEMM_WAVES == 8
-  // Two waves per SIMD: the other wave hides the fragment reads, so they are read in the
-  // step that uses them (one fragment set keeps the wave within 256 registers).  Step k
-  // waits for stage k and refills the buffer read in step k - 1 with stage k + 3.
-  Frags f;
+  // Two waves per SIMD, 256 registers each: fragments are handled one chunk (two of the four
+  // MFMA substeps) at a time.  The first chunk of stage k + 1 is read during step k and the
+  // second chunk of stage k at the start of step k, so the matrix instructions never wait for
+  // LDS.  Step k waits for stage k + 1 (stage k + 2 may stay in flight), then a plain
+  // s_barrier makes every wave's transfers visible and guarantees that buffer (k - 1) % 4,
+  // refilled now with stage k + 3, is no longer read.
+  Half f0, f1, g0;
   issue_stage(st0, ra, rb, rowB, 0, wave, lane);
   issue_stage(st1, ra, rb, rowB, 1, wave, lane);
   issue_stage(st2, ra, rb, rowB, 2, wave, lane);
-#define CONVROT_STEP(K, CUR, REFILL)                                                \
-  wait_own_stage();                                                                 \
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerWave));  // vmcnt: stage 0 landed
+  __builtin_amdgcn_s_barrier();
+  read_half(st0, 0, wn, wm, lane, f0);
+#define CONVROT_STEP(K, CUR, NEXT, REFILL)                                          \
+  __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerWave); /* vmcnt: stage K + 1 landed */  \
+  __builtin_amdgcn_s_waitcnt(0xC07F);               /* lgkmcnt(0) */                \
   __builtin_amdgcn_s_barrier();                                                     \
   issue_stage(REFILL, ra, rb, rowB, (K) + 3, wave, lane);                           \
-  read_frags(CUR, wn, wm, lane, f);                                                 \
-  mma_frags(f, acc);
+  read_half(CUR, 1, wn, wm, lane, f1);                                              \
+  read_half(NEXT, 0, wn, wm, lane, g0);                                             \
+  mma_half(f0, acc);                                                                \
+  mma_half(f1, acc);                                                                \
+  f0 = g0;
   int k = 0;
   for (; k + 4 <= nsteps; k += 4) {
-    CONVROT_STEP(k, st0, st3)
-    CONVROT_STEP(k + 1, st1, st0)
-    CONVROT_STEP(k + 2, st2, st1)
-    CONVROT_STEP(k + 3, st3, st2)
+    CONVROT_STEP(k, st0, st1, st3)
+    CONVROT_STEP(k + 1, st1, st2, st0)
+    CONVROT_STEP(k + 2, st2, st3, st1)
+    CONVROT_STEP(k + 3, st3, st0, st2)
   }
   if (k < nsteps) {
-    CONVROT_STEP(k, st0, st3)
+    CONVROT_STEP(k, st0, st1, st3)
     if (k + 1 < nsteps) {
-      CONVROT_STEP(k + 1, st1, st0)
+      CONVROT_STEP(k + 1, st1, st2, st0)
       if (k + 2 < nsteps) {
-        CONVROT_STEP(k + 2, st2, st1)
+        CONVROT_STEP(k + 2, st2, st3, st1)
       }
     }
   }
