@@ -10,4 +10,6 @@ from .convrot_oracle import (  # noqa: F401
     pack_int4, padded_k, quantize, quantize_weight, reference_linear_fp64,
     regular_hadamard, rotate_groups, rotate_quantize, row_scales, to_f32, unpack_int4,
     w4a4_linear_from_codes, zero_pad_columns,
+    INT8_QMAX, INT8_QMIN, rotate_quantize_int8, quantize_weight_int8, w8a8_linear_from_codes,
+    convlinear8bit,
 )

@@ -59,6 +59,8 @@ import numpy as np
 
 INT4_QMAX = 7       # symmetric int4: codes in [-8, 7], scale = absmax / 7
 INT4_QMIN = -8
+INT8_QMAX = 127     # symmetric int8 ([HSWQ]): codes in [-128, 127], scale = absmax / 127
+INT8_QMIN = -128
 
 
 # --------------------------------------------------------------------------
@@ -200,6 +202,21 @@ def quantize_weight(w: np.ndarray, g: int) -> dict:
     return rotate_quantize(w, g)
 
 
+def rotate_quantize_int8(a: np.ndarray, g: int) -> dict:
+    """The INT8 variant ([HSWQ] "Hadamard Orthogonal Rotation": scale = max|rotated| / 127,
+    codes = round(rotated / scale)) on the same group-wise regular rotation; one int8 code
+    per element, rows of K' codes."""
+    yf = to_f32(rotate_groups(a, g))
+    s = row_scales(yf, INT8_QMAX)
+    q = quantize(yf, s, INT8_QMAX, INT8_QMIN)
+    return {"yf": yf, "scale": s, "codes": q}
+
+
+def quantize_weight_int8(w: np.ndarray, g: int) -> dict:
+    """Offline INT8 weight path (per output channel)."""
+    return rotate_quantize_int8(w, g)
+
+
 # --------------------------------------------------------------------------
 # W4A4 GEMM and dequantization ([KITCHEN] review of int4_linear; [PAPER] Abstract)
 # --------------------------------------------------------------------------
@@ -207,7 +224,7 @@ def int_gemm(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
     """acc[m, n] = sum_k qx[m, k] qw[n, k] exactly (x @ w^T).
 
     The float64 matmul is exact: every partial sum is an integer of magnitude
-    at most 64 K' < 2^53.
+    at most 64 K' (int4 codes) or 16384 K' (int8 codes), below 2^53.
     """
     acc = np.asarray(qx, dtype=np.float64) @ np.asarray(qw, dtype=np.float64).T
     return acc.astype(np.int64)
@@ -226,8 +243,11 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def dequantize(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray,
                bias: Optional[np.ndarray] = None) -> np.ndarray:
-    """out = bf16(fp32(fp32(fp32(acc) * sx[m]) * sw[n]) [+ fp32 bias[n]]), as bf16 bits."""
-    z = np.asarray(acc, dtype=np.float32)       # exact: |acc| <= 64 K' < 2^24
+    """out = bf16(fp32(fp32(fp32(acc) * sx[m]) * sw[n]) [+ fp32 bias[n]]), as bf16 bits.
+
+    fp32(acc) is exact for int4 codes (|acc| <= 64 K' < 2^24); for int8 codes at large K' it
+    is the round-to-nearest-even conversion of the exact integer."""
+    z = np.asarray(acc, dtype=np.float32)
     z = (z * np.asarray(sx, dtype=np.float32)[:, None]).astype(np.float32)
     z = (z * np.asarray(sw, dtype=np.float32)[None, :]).astype(np.float32)
     if bias is not None:
@@ -245,6 +265,20 @@ def convlinear4bit(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], g: 
     xr = rotate_quantize(x, g)
     wr = quantize_weight(w, g)
     lin = w4a4_linear_from_codes(xr["codes"], xr["scale"], wr["codes"], wr["scale"], bias)
+    return {"x": xr, "w": wr, **lin}
+
+
+def w8a8_linear_from_codes(qx, sx, qw, sw, bias=None) -> dict:
+    """INT8 GEMM (exact int32 sums: |acc| <= 16384 K' < 2^31 for K' <= 65536) + dequant."""
+    acc = int_gemm(qx, qw)
+    return {"acc": acc, "out_bits": dequantize(acc, sx, sw, bias)}
+
+
+def convlinear8bit(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], g: int) -> dict:
+    """The W8A8 forward pass: the same rotation, int8 codes on both sides."""
+    xr = rotate_quantize_int8(x, g)
+    wr = quantize_weight_int8(w, g)
+    lin = w8a8_linear_from_codes(xr["codes"], xr["scale"], wr["codes"], wr["scale"], bias)
     return {"x": xr, "w": wr, **lin}
 
 

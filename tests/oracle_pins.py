@@ -411,4 +411,90 @@ def pin_int4_linear_semantics(o):
     assert np.array_equal(r["acc"], acc)
 
 
+# ---------------------------------------------------------------- INT8 variant ([HSWQ])
+def pin_int8_round_trip(o):
+    """Rows 2^e * (integers in [-127, 127]) with |127| present come back exactly, and the
+    row scale is 2^e (127 * 2^e / 127 is exact)."""
+    rng = np.random.default_rng(20)
+    ints = rng.integers(-127, 128, size=(6, 96))
+    ints[:, 5] = 127
+    ints[3, 5] = -127
+    e = rng.integers(-12, 6, size=6)
+    s = np.exp2(e).astype(np.float32)
+    yf = (ints * s[:, None].astype(np.float64)).astype(np.float32)
+    r = o.row_scales(yf, o.INT8_QMAX)
+    assert np.array_equal(r, s)
+    assert np.array_equal(o.quantize(yf, r, o.INT8_QMAX, o.INT8_QMIN), ints.astype(np.int8))
+
+
+def pin_int8_rotate_quantize(o):
+    """The INT8 path is the same rotation with q_max 127: scale = fp32(absmax / 127), the
+    absmax element maps to +-127, codes in [-127, 127], and |code - rotated/scale| <= 1/2."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((9, 300)).astype(np.float32)
+    x[2] *= 40.0
+    for g in (16, 64, 256):
+        r = o.rotate_quantize_int8(x, g)
+        yf = o.to_f32(o.rotate_groups(x, g))
+        assert np.array_equal(r["yf"], yf)
+        amax = np.max(np.abs(yf), axis=1)
+        assert np.array_equal(r["scale"], (amax / np.float32(127)).astype(np.float32))
+        q = r["codes"].astype(np.int64)
+        assert q.shape == yf.shape and q.min() >= -127 and q.max() <= 127
+        am = np.argmax(np.abs(yf), axis=1)
+        assert np.array_equal(np.abs(q[np.arange(9), am]), np.full(9, 127))
+        z = yf.astype(np.float64) / r["scale"][:, None].astype(np.float64)
+        assert np.max(np.abs(q - z)) <= 0.5 + 1e-6
+        # the same rotation and scales, only q_max differs from the int4 path
+        r4 = o.rotate_quantize(x, g)
+        assert np.array_equal(r4["yf"], r["yf"])
+        assert np.array_equal(r4["scale"], (amax / np.float32(7)).astype(np.float32))
+
+
+def pin_int8_gemm_brute_force(o):
+    """Exact int32 sums over the full int8 range, by a triple loop; the largest magnitude
+    16384 K' still fits int32 at K' = 65536 - 128."""
+    rng = np.random.default_rng(22)
+    for M, N, K in ((4, 3, 64), (2, 5, 32)):
+        qx = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        qw = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+        acc = o.int_gemm(qx, qw)
+        for m in range(M):
+            for n in range(N):
+                assert acc[m, n] == sum(int(qx[m, k]) * int(qw[n, k]) for k in range(K))
+    K = 65536 - 128
+    full = np.full((1, K), -128, dtype=np.int8)
+    assert o.int_gemm(full, full)[0, 0] == 16384 * K < 2 ** 31
+
+
+def pin_int8_dequant_rounds_large_sums(o):
+    """fp32(acc) is the round-to-nearest-even conversion once |acc| >= 2^24."""
+    acc = np.array([[2 ** 24 + 1, 2 ** 24 + 3, -(2 ** 25 + 2), 127 * 127 * 3072]], dtype=np.int64)
+    one = np.ones(1, dtype=np.float32)
+    ones = np.ones(4, dtype=np.float32)
+    got = o.bf16_bits_to_f32(o.dequantize(acc, one, ones)).astype(np.float64)
+    want = [float(np.float32(v)) for v in acc[0]]            # IEEE RNE int -> fp32
+    import torch
+    want = torch.tensor(want, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got[0], want)
+    assert float(np.float32(2 ** 24 + 1)) == 2.0 ** 24 and float(np.float32(2 ** 24 + 3)) == 2.0 ** 24 + 4
+
+
+def pin_int8_end_to_end_closed_form(o):
+    """Constant rows: codes +-127, scales |c|/127, acc = 127^2 K sign, out = bf16(K c d)."""
+    import torch
+    for g, K, c, d in ((16, 64, 2.0, 0.5), (256, 512, -4.0, 0.25), (64, 128, 1.0, -1.0)):
+        x = np.full((2, K), c)
+        w = np.full((3, K), d)
+        r = o.convlinear8bit(x, w, None, g)
+        assert np.all(np.abs(r["x"]["codes"]) == 127) and np.all(np.abs(r["w"]["codes"]) == 127)
+        assert np.all(r["x"]["scale"] == np.float32(abs(c) / 127))
+        assert np.all(r["acc"] == 127 * 127 * K * int(np.sign(c) * np.sign(d)))
+        z = np.float32(np.float32(np.float32(127 * 127 * K * np.sign(c * d)) * np.float32(abs(c) / 127))
+                       * np.float32(abs(d) / 127))
+        want = torch.tensor([float(z)], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
+        assert np.all(r["out_bits"] == np.uint16(want.numpy().view(np.uint16)[0]))
+        assert abs(float(z) - K * c * d) <= 1e-5 * abs(K * c * d)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -104,6 +104,12 @@ def _bf16_truncate(z):
     return (u >> np.uint32(16)).astype(np.uint16)
 
 
+def _rotate_quantize_int8_scale7(a, g):
+    r = _orig["rotate_quantize_int8"](a, g)
+    s = _orig["row_scales"](r["yf"], 7)
+    return {"yf": r["yf"], "scale": s, "codes": _orig["quantize"](r["yf"], s, 127, -128)}
+
+
 MUTATIONS = {
     "sylvester_base": ({"base_regular_hadamard": _sylvester_base}, ["pin_regular"]),
     "negated_base": ({"base_regular_hadamard": lambda: -_orig["base_regular_hadamard"]()},
@@ -123,6 +129,9 @@ MUTATIONS = {
     "bias_before_scale": ({"dequantize": _dequant_bias_first}, ["pin_end_to_end_closed_form", "pin_int4_linear_semantics"]),
     "dropped_weight_scale": ({"dequantize": _dequant_no_wscale}, ["pin_int4_linear_semantics"]),
     "bf16_truncation": ({"f32_to_bf16_bits": _bf16_truncate}, ["pin_bf16_rounding_vs_torch"]),
+    "int8_qmax_128": ({"INT8_QMAX": 128}, ["pin_int8_round_trip", "pin_int8_rotate_quantize"]),
+    "int8_int4_scale": ({"rotate_quantize_int8": _rotate_quantize_int8_scale7},
+                        ["pin_int8_rotate_quantize", "pin_int8_end_to_end_closed_form"]),
 }
 
 
