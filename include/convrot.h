@@ -151,6 +151,51 @@ CONVROT_API int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, i
                         const uint8_t* wq, const float* ws, int64_t N, const void* bias,
                         void* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * INT8 variant (W8A8): the same group-wise regular rotation with 8-bit symmetric codes
+ * ([HSWQ] "Hadamard Orthogonal Rotation": per-row scale = absmax / 127, codes =
+ * round(rotated / scale); [AUTHOR]: the rotation is independent of the code format).
+ * Codes are int8, one per element, row stride K' bytes; scale = fp32(absmax / 127) (exact
+ * absmax, bit-identical to the definition); codes may differ by one from the definition
+ * where the quotient lies within a few ulp of a rounding tie.  The sums are exact int32
+ * (|acc| <= 16384 K' < 2^31); y = bf16( fp32( fp32( fp32(acc) * xs[m] ) * ws[n] ) + bias[n] ),
+ * fp32(acc) rounding to nearest even once |acc| >= 2^24.
+ * --------------------------------------------------------------------------------------- */
+
+/* Online activation path, INT8 codes: as convrot_rotate_quant_act, with
+ *   xq  device, int8 [M][K'] codes, 16-byte aligned.
+ * K' limits as for int4 codes except: g = 1024 with bf16 input, K' <= 53248; fp32 input,
+ * K' <= 30720 (g = 64, 256) or 28672 (g = 1024).  Each row's packed codes and raw input
+ * windows are staged in the workgroup's LDS, and int8 codes take twice the room of int4.
+ * M = 0 is a no-op.  Errors: GROUP, UNSUPPORTED, SHAPE, NULL, DTYPE, ALIGN, HIP. */
+CONVROT_API int convrot_rotate_quant_act_i8(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                int64_t ldx, int64_t g, int8_t* xq, float* xs, float* xrot,
+                                void* stream);
+
+/* Offline INT8 weight path: wq int8 [N][K'] (16-byte aligned), ws fp32 [N]. */
+CONVROT_API int convrot_quant_weight_i8(const void* w, int32_t w_dtype, int64_t N, int64_t K,
+                            int64_t g, int8_t* wq, float* ws, void* stream);
+
+/* W8A8 GEMM with fused dequantization (int8 matrix cores, no unpacking):
+ *   xq [M][Kp], wq [N][Kp] int8 (16-byte aligned), xs fp32 [M], ws fp32 [N], bias bf16 [N]
+ *   or NULL, y bf16 [M][N] (4-byte aligned); Kp a positive multiple of 16, <= CONVROT_MAX_KP;
+ *   acc_dbg int32 [M][N] (16-byte aligned) or NULL, as for convrot_w4a4_gemm.
+ * M = 0 or N = 0 is a no-op.  Errors: SHAPE, NULL, ALIGN, UNSUPPORTED, HIP. */
+CONVROT_API int convrot_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
+                      const void* bias, int64_t M, int64_t N, int64_t Kp, void* y,
+                      int32_t* acc_dbg, void* stream);
+
+/* Bytes of device workspace convrot_w8a8_linear needs: codes M*K' and scales 4*M, each
+ * rounded up to 256 bytes.  Returns 0 for an invalid g or shape. */
+CONVROT_API size_t convrot_w8a8_workspace_bytes(int64_t M, int64_t K, int64_t g);
+
+/* The W8A8 forward pass: rotate + quantize x to int8 codes in the workspace, then the W8A8
+ * GEMM against wq int8 [N][K'] / ws [N] (from convrot_quant_weight_i8 with the same g and K),
+ * writing y bf16 [M][N].  Arguments and errors as for convrot_w4a4_linear. */
+CONVROT_API int convrot_w8a8_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t g,
+                        const int8_t* wq, const float* ws, int64_t N, const void* bias,
+                        void* y, void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -8,6 +8,8 @@ from ._lib import (  # noqa: F401
     convrot_is_power_of_4, convrot_make_rht, convrot_padded_k, convrot_quant_weight,
     convrot_rotate_quant_act, convrot_status_string, convrot_version, convrot_w4a4_gemm,
     convrot_w4a4_linear, convrot_w4a4_workspace_bytes, load_library,
+    convrot_quant_weight_i8, convrot_rotate_quant_act_i8, convrot_w8a8_gemm,
+    convrot_w8a8_linear, convrot_w8a8_workspace_bytes,
 )
 from .linear import ConvLinear4bit  # noqa: F401
 
@@ -15,5 +17,6 @@ __all__ = [
     "ConvLinear4bit", "ConvRotError", "load_library", "convrot_status_string", "convrot_version",
     "convrot_padded_k", "convrot_is_power_of_4", "convrot_make_rht", "convrot_rotate_quant_act",
     "convrot_quant_weight", "convrot_w4a4_gemm", "convrot_w4a4_workspace_bytes",
-    "convrot_w4a4_linear",
+    "convrot_w4a4_linear", "convrot_rotate_quant_act_i8", "convrot_quant_weight_i8",
+    "convrot_w8a8_gemm", "convrot_w8a8_workspace_bytes", "convrot_w8a8_linear",
 ]

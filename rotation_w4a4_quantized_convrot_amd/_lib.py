@@ -42,6 +42,13 @@ SIGNATURES = {
     "convrot_w4a4_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "convrot_w4a4_linear": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp]),
+    "convrot_rotate_quant_act_i8": (_c_int, [_vp, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
+                                             _vp]),
+    "convrot_quant_weight_i8": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "convrot_w8a8_gemm": (_c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "convrot_w8a8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "convrot_w8a8_linear": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
+                                     ctypes.c_size_t, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -220,6 +227,94 @@ def convrot_w4a4_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Ten
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     st = load_library().convrot_w4a4_linear(
+        _ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(ws), N, _ptr(bias), _ptr(y),
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    _check(st, g)
+    return y
+
+
+# ----------------------------------------------------------------- INT8 (W8A8) variant
+def convrot_w8a8_workspace_bytes(M: int, K: int, g: int) -> int:
+    return int(load_library().convrot_w8a8_workspace_bytes(int(M), int(K), int(g)))
+
+
+def convrot_rotate_quant_act_i8(x: torch.Tensor, g: int, xq: Optional[torch.Tensor] = None,
+                                xs: Optional[torch.Tensor] = None,
+                                xrot: Optional[torch.Tensor] = None, want_rotated: bool = False):
+    """x [M, K] (bf16/fp32, row stride x.stride(0)) -> (xq int8 [M, K'], xs fp32 [M][, xrot])."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    Kp = convrot_padded_k(K, g)
+    dev = _require_device(x, xq, xs, xrot)
+    if xq is None:
+        xq = torch.empty((M, Kp), dtype=torch.int8, device=dev)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=dev)
+    if xrot is None and want_rotated:
+        xrot = torch.empty((M, Kp), dtype=torch.float32, device=dev)
+    st = load_library().convrot_rotate_quant_act_i8(
+        _ptr(x), _dtype_code(x), M, K, x.stride(0), g, _ptr(xq), _ptr(xs), _ptr(xrot),
+        _stream(dev))
+    _check(st, g)
+    return (xq, xs, xrot) if xrot is not None else (xq, xs)
+
+
+def convrot_quant_weight_i8(w: torch.Tensor, g: int, wq: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """w [N, K] contiguous (bf16/fp32) -> (wq int8 [N, K'], ws fp32 [N])."""
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D tensor")
+    N, K = w.shape
+    Kp = convrot_padded_k(K, g)
+    dev = _require_device(w, wq, ws)
+    if wq is None:
+        wq = torch.empty((N, Kp), dtype=torch.int8, device=dev)
+    if ws is None:
+        ws = torch.empty((N,), dtype=torch.float32, device=dev)
+    st = load_library().convrot_quant_weight_i8(_ptr(w), _dtype_code(w), N, K, g, _ptr(wq),
+                                                _ptr(ws), _stream(dev))
+    _check(st, g)
+    return wq, ws
+
+
+def convrot_w8a8_gemm(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
+                      bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                      want_acc: bool = False):
+    """int8 GEMM + dequant: y bf16 [M, N] (and the int32 sums [M, N] if want_acc)."""
+    M, Kp = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != Kp:
+        raise ValueError("xq and wq must have the same depth")
+    if bias is not None and bias.dtype != torch.bfloat16:
+        raise TypeError("bias must be bfloat16")
+    dev = _require_device(xq, xs, wq, ws, bias, y)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
+    st = load_library().convrot_w8a8_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(bias), M, N,
+                                          Kp, _ptr(y), _ptr(acc), _stream(dev))
+    _check(st)
+    return (y, acc) if want_acc else y
+
+
+def convrot_w8a8_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Tensor,
+                        bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """W8A8 ConvRot forward: x [M, K] contiguous -> y bf16 [M, N]."""
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    M, K = x.shape
+    N = wq.shape[0]
+    if bias is not None and bias.dtype != torch.bfloat16:
+        raise TypeError("bias must be bfloat16")
+    dev = _require_device(x, wq, ws, bias, y, workspace)
+    need = convrot_w8a8_workspace_bytes(M, K, g)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    st = load_library().convrot_w8a8_linear(
         _ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(ws), N, _ptr(bias), _ptr(y),
         _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, g)

@@ -16,12 +16,18 @@ bool kernel_group(int64_t g) { return g == 16 || g == 64 || g == 256 || g == 102
 
 // Longest padded row the rotate+quantize kernel holds on chip: at most 16 waves x 64 lanes x
 // the elements per lane of its window layout (16 for g = 16, 32 for g = 64 and 256, 64 for
-// 1024), and the workgroup's LDS staging within 160 KiB (g = 1024: 15 waves for bf16, 8 for
-// fp32 inputs).
-int64_t max_row_kp(int64_t g, int32_t dtype) {
+// 1024), and the workgroup's LDS staging (raw input window + packed codes per window) within
+// 160 KiB: g = 1024 fits 15 waves for bf16 input and int4 codes, 13 for bf16 and int8 codes,
+// 8 for fp32 and int4 and 7 for fp32 and int8; g = 64 and 256 with fp32 input and int8 codes
+// fit 15 waves.
+int64_t max_row_kp(int64_t g, int32_t dtype, int qbits = 4) {
+  const bool f32 = dtype == CONVROT_F32;
   if (g == 16) return 16384;
-  if (g == 1024) return dtype == CONVROT_F32 ? 32768 : 61440;
-  return 32768;
+  if (g == 1024) {
+    if (qbits == 8) return f32 ? 28672 : 53248;
+    return f32 ? 32768 : 61440;
+  }
+  return f32 && qbits == 8 ? 30720 : 32768;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -48,7 +54,8 @@ int status_of(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_
 
 // Validates a rotate+quantize call; on success *kp_out = K'.
 int validate_rq(const void* x, int32_t dtype, int64_t M, int64_t K, int64_t ldx, int64_t g,
-                const uint8_t* q, const float* s, const float* xrot, int64_t* kp_out) {
+                const uint8_t* q, const float* s, const float* xrot, int64_t* kp_out,
+                int qbits = 4) {
   int st = check_group(g);
   if (st != CONVROT_OK) return st;
   if (elem_size(dtype) == 0) return CONVROT_ERR_DTYPE;
@@ -56,7 +63,7 @@ int validate_rq(const void* x, int32_t dtype, int64_t M, int64_t K, int64_t ldx,
     return CONVROT_ERR_SHAPE;
   const int64_t kp = convrot_padded_k(K, g);
   if (kp < 0) return (int)kp;
-  if (kp > max_row_kp(g, dtype)) return CONVROT_ERR_UNSUPPORTED;
+  if (kp > max_row_kp(g, dtype, qbits)) return CONVROT_ERR_UNSUPPORTED;
   if (M == 0) {
     *kp_out = kp;
     return CONVROT_OK;
@@ -95,7 +102,9 @@ const char* convrot_status_string(int status) {
     case CONVROT_ERR_GROUP: return "group size is not a power of 4 (>= 4)";
     case CONVROT_ERR_UNSUPPORTED:
       return "unsupported: group size must be 16, 64, 256 or 1024, and K' at most 16384 "
-             "(g = 16), 32768 (g = 64, 256) or 61440 (g = 1024; 32768 for fp32 input)";
+             "(g = 16), 32768 (g = 64, 256) or 61440 (g = 1024; 32768 for fp32 input); "
+             "with int8 codes 53248 (g = 1024, bf16), 30720 "
+             "(g = 64, 256, fp32) or 28672 (g = 1024, fp32)";
     case CONVROT_ERR_SHAPE: return "invalid shape (M, N >= 0, K >= 1, ld >= K, no overflow)";
     case CONVROT_ERR_NULL: return "a required pointer is NULL";
     case CONVROT_ERR_DTYPE: return "unknown dtype code";
@@ -139,8 +148,77 @@ int convrot_rotate_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t 
   const int st = validate_rq(x, x_dtype, M, K, ldx, g, xq, xs, xrot, &kp);
   if (st != CONVROT_OK || M == 0) return st;
   const int vec = vector_width(x, ldx * elem_size(x_dtype));
-  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp, vec, xq, xs,
+  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp, 4, vec, xq,
+                                                xs, xrot, static_cast<hipStream_t>(stream)));
+}
+
+int convrot_rotate_quant_act_i8(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                int64_t ldx, int64_t g, int8_t* xq, float* xs, float* xrot,
+                                void* stream) {
+  int64_t kp = 0;
+  uint8_t* q = reinterpret_cast<uint8_t*>(xq);
+  const int st = validate_rq(x, x_dtype, M, K, ldx, g, q, xs, xrot, &kp, 8);
+  if (st != CONVROT_OK || M == 0) return st;
+  const int vec = vector_width(x, ldx * elem_size(x_dtype));
+  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp, 8, vec, q, xs,
                                                 xrot, static_cast<hipStream_t>(stream)));
+}
+
+int convrot_quant_weight_i8(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t g,
+                            int8_t* wq, float* ws, void* stream) {
+  return convrot_rotate_quant_act_i8(w, w_dtype, N, K, K, g, wq, ws, nullptr, stream);
+}
+
+int convrot_w8a8_gemm(const int8_t* xq, const float* xs, const int8_t* wq, const float* ws,
+                      const void* bias, int64_t M, int64_t N, int64_t Kp, void* y,
+                      int32_t* acc_dbg, void* stream) {
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(xq);
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(wq);
+  const int st = validate_gemm(xb, xs, wb, ws, bias, M, N, Kp, y, acc_dbg);
+  if (st != CONVROT_OK || M == 0 || N == 0) return st;
+  return status_of(convrot::launch_w8a8_gemm(xb, xs, wb, ws, static_cast<const uint16_t*>(bias),
+                                             M, N, Kp, static_cast<uint16_t*>(y), acc_dbg,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+size_t convrot_w8a8_workspace_bytes(int64_t M, int64_t K, int64_t g) {
+  if (M < 0 || M > INT32_MAX) return 0;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return 0;
+  return round256((size_t)M * (size_t)kp) + round256((size_t)M * 4);
+}
+
+int convrot_w8a8_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t g,
+                        const int8_t* wq, const float* ws, int64_t N, const void* bias, void* y,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_group(g);
+  if (st != CONVROT_OK) return st;
+  if (elem_size(x_dtype) == 0) return CONVROT_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 1 || M > INT32_MAX || N > INT32_MAX) return CONVROT_ERR_SHAPE;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return (int)kp;
+  if (kp > max_row_kp(g, x_dtype, 8)) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (x == nullptr || wq == nullptr || ws == nullptr || y == nullptr || workspace == nullptr)
+    return CONVROT_ERR_NULL;
+  if (!aligned(workspace, 256)) return CONVROT_ERR_ALIGN;
+  if (ws_bytes < convrot_w8a8_workspace_bytes(M, K, g)) return CONVROT_ERR_WORKSPACE;
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(xq + round256((size_t)M * (size_t)kp));
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(wq);
+  int64_t kp_rq = 0;
+  st = validate_rq(x, x_dtype, M, K, K, g, xq, xs, nullptr, &kp_rq, 8);
+  if (st != CONVROT_OK) return st;
+  st = validate_gemm(xq, xs, wb, ws, bias, M, N, kp, y, nullptr);
+  if (st != CONVROT_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int vec = vector_width(x, K * elem_size(x_dtype));
+  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, 8, vec, xq, xs,
+                                              nullptr, s);
+  if (e != hipSuccess) return CONVROT_ERR_HIP;
+  e = convrot::launch_w8a8_gemm(xq, xs, wb, ws, static_cast<const uint16_t*>(bias), M, N, kp,
+                                static_cast<uint16_t*>(y), nullptr, s);
+  return status_of(e);
 }
 
 int convrot_quant_weight(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t g,
@@ -190,7 +268,7 @@ int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
   if (st != CONVROT_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int vec = vector_width(x, K * elem_size(x_dtype));
-  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, vec, xq, xs,
+  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, 4, vec, xq, xs,
                                               nullptr, s);
   if (e != hipSuccess) return CONVROT_ERR_HIP;
   const int gvec = ((kp / 2) % 16 == 0) ? 16 : 8;

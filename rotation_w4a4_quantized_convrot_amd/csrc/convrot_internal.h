@@ -6,11 +6,13 @@
 
 namespace convrot {
 
-// Launches the fused pad + group-wise RHT + per-row absmax + int4 quantize + pack kernel
-// on rows [0, M) of x (row stride ldx elements).  g in {16, 64, 256, 1024}; Kp = K' <= 65536.
-// x_dtype: 0 = fp32, 1 = bf16.  vec_bytes: widest aligned vector load (2, 4, 8 or 16 bytes).
+// Launches the fused pad + group-wise RHT + per-row absmax + quantize + pack kernel on rows
+// [0, M) of x (row stride ldx elements).  g in {16, 64, 256, 1024}; Kp = K' <= 65536.
+// x_dtype: 0 = fp32, 1 = bf16.  qbits: 4 (int4 codes, K'/2 bytes per row, scale = max/7) or
+// 8 (int8 codes, K' bytes per row, scale = max/127).  vec_bytes: widest aligned vector load
+// (2, 4, 8 or 16 bytes).
 hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                               int g, int64_t Kp, int vec_bytes, uint8_t* q, float* s,
+                               int g, int64_t Kp, int qbits, int vec_bytes, uint8_t* q, float* s,
                                float* xrot, hipStream_t stream);
 
 // Launches the W4A4 GEMM with the fused dequant epilogue.  vec_bytes: 16 when the packed
@@ -19,6 +21,12 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             const float* ws, const uint16_t* bias, int64_t M, int64_t N,
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, int vec_bytes,
                             hipStream_t stream);
+
+// Launches the W8A8 GEMM (int8 codes, K' bytes per row, exact int32 sums) with the same
+// fused dequant epilogue.  Kp must be a multiple of 16.
+hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq,
+                            const float* ws, const uint16_t* bias, int64_t M, int64_t N,
+                            int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream);
 
 // Small launch helper that returns the launch status instead of relying on hipGetLastError.
 template <typename... KArgs, typename... Args>

@@ -358,7 +358,7 @@ __device__ __forceinline__ float candidate_slack() {
 // prefetching block b + gridDim.x into registers while block b is processed.  One workgroup
 // barrier per block: per-row maxima meet in LDS through atomics on four rotating buffers;
 // the row scale (which needs the exact maximum) is stored one iteration later.
-template <int G, typename TIn, int VEC>
+template <int G, typename TIn, int VEC, int QB>
 __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__ x, int M, int K,
                                                          long ldx, int Kp, int W, int R,
                                                          int nblocks, uint8_t* __restrict__ q,
@@ -366,7 +366,13 @@ __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__
                                                          float* __restrict__ xrot) {
   constexpr int L = Geo<G>::L, E = Geo<G>::E, C = E / 8, U = 64 / L;
   constexpr int ES = sizeof(TIn);
-  constexpr int kWinBytes = G / 2, kLaneBytes = E / 2;
+  // QB = code width: 4 (int4, two codes per byte) or 8 (int8, one code per byte).
+  constexpr int kWinBytes = G * QB / 8, kLaneBytes = E * QB / 8;
+  constexpr float kQmax = QB == 4 ? 7.0f : 127.0f;
+  // fma(y, qmax/absmax, kMagic) rounds half-to-even and leaves, in the low mantissa bits,
+  // code + 8 (int4: one nibble) or the two's-complement code (int8: one byte).
+  constexpr float kMagic = QB == 4 ? 12582920.0f : 12582912.0f;
+  const long rowQ = long(Kp) * QB / 8;  // bytes of codes per row
   extern __shared__ uint32_t smem[];
   uint32_t* red = smem;  // [4 buffers][2 (fp32 max, exact max)][R], float bits
   const int nwaves = blockDim.x >> 6;
@@ -390,9 +396,9 @@ __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__
     partial |= slot_used && col < K && col + 8 > K;
   }
   const bool any_partial = __ballot(partial) != 0;
-  const uint32_t qoff = slot_used ? uint32_t(rloc * (Kp / 2) + j * kWinBytes + lu * kLaneBytes) : kOob;
+  const uint32_t qoff = slot_used ? uint32_t(rloc * rowQ + j * kWinBytes + lu * kLaneBytes) : kOob;
   const long blk_in = long(R) * ldx, valid_in = long(M - 1) * ldx + K;
-  const long blk_out = long(R) * (Kp / 2), total_out = long(M) * (Kp / 2);
+  const long blk_out = long(R) * rowQ, total_out = long(M) * rowQ;
 
   for (int i = tid; i < 8 * R; i += blockDim.x) red[i] = 0u;
 
@@ -464,7 +470,7 @@ __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__
 
     // Scale of the previous block: its exact maxima are complete (they precede this barrier).
     if (prev_m >= 0 && lu == 0 && j == 0)
-      s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / 7.0f;
+      s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / kQmax;
     {
       uint32_t* zb = red + ((it + 2) & 3) * 2 * R;
       for (int i = tid; i < 2 * R; i += blockDim.x) zb[i] = 0u;
@@ -472,23 +478,37 @@ __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__
 
     // Codes use the fp32 maximum; they agree with the exact one except at rounding ties.
     const float mrow = slot_used ? __uint_as_float(rmax[rloc < R ? rloc : 0]) : 0.0f;
-    const float inv = mrow > 0.0f ? 7.0f / mrow : 0.0f;
-    uint32_t packed[C];
+    const float inv = mrow > 0.0f ? kQmax / mrow : 0.0f;
+    uint32_t packed[C][QB / 4];  // the chunk's 8 codes: one dword (int4) or two (int8)
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       uint32_t bits[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        bits[e] = __float_as_uint(__builtin_fmaf(v[8 * r + e], inv, 12582920.0f));
-      const uint32_t lo = (bits[3] << 12) | ((bits[2] << 8) | ((bits[1] << 4) | bits[0]));
-      const uint32_t hi = (bits[7] << 12) | ((bits[6] << 8) | ((bits[5] << 4) | bits[4]));
-      packed[r] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
+        bits[e] = __float_as_uint(__builtin_fmaf(v[8 * r + e], inv, kMagic));
+      if constexpr (QB == 4) {
+        const uint32_t lo = (bits[3] << 12) | ((bits[2] << 8) | ((bits[1] << 4) | bits[0]));
+        const uint32_t hi = (bits[7] << 12) | ((bits[6] << 8) | ((bits[5] << 4) | bits[4]));
+        packed[r][0] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ 0x88888888u;
+      } else {  // low byte of each: two byte gathers, then one merge per four codes
+        const uint32_t p01 = __builtin_amdgcn_perm(bits[1], bits[0], 0x0C0C0400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(bits[3], bits[2], 0x0C0C0400u);
+        const uint32_t p45 = __builtin_amdgcn_perm(bits[5], bits[4], 0x0C0C0400u);
+        const uint32_t p67 = __builtin_amdgcn_perm(bits[7], bits[6], 0x0C0C0400u);
+        packed[r][0] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        packed[r][1] = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
+      }
     }
     // Transpose the unit's packed window through this wave's LDS slice so every lane
     // stores contiguous bytes (wave-local: LDS operations of one wave complete in order).
     uint8_t* ub = stage + (wave * U + unit) * kWinBytes;
 #pragma unroll
-    for (int r = 0; r < C; ++r) reinterpret_cast<uint32_t*>(ub)[chunk_of<G>(lu, r)] = packed[r];
+    for (int r = 0; r < C; ++r) {
+      if constexpr (QB == 4)
+        reinterpret_cast<uint32_t*>(ub)[chunk_of<G>(lu, r)] = packed[r][0];
+      else
+        reinterpret_cast<uint2*>(ub)[chunk_of<G>(lu, r)] = make_uint2(packed[r][0], packed[r][1]);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -551,7 +571,7 @@ __global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__
   }
   __syncthreads();
   if (prev_m >= 0 && lu == 0 && j == 0)
-    s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / 7.0f;
+    s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / kQmax;
 }
 
 struct RqPlan {
@@ -562,16 +582,17 @@ struct RqPlan {
 // the workgroup's LDS (per-row reduction slots + per-wave staging) within the 160 KiB of a CU.
 constexpr size_t kMaxLds = 160 * 1024;
 
-size_t rq_shmem(int R, int waves, int U, int G, int esize) {
-  return size_t((8 * R + 3) & ~3) * 4 + size_t(waves) * U * (G / 2) + size_t(waves) * U * G * esize;
+size_t rq_shmem(int R, int waves, int U, int G, int esize, int qb) {
+  return size_t((8 * R + 3) & ~3) * 4 + size_t(waves) * U * (G * qb / 8) +
+         size_t(waves) * U * G * esize;
 }
 
-RqPlan plan_rows(int W, int U, int G, int esize) {
+RqPlan plan_rows(int W, int U, int G, int esize, int qb) {
   RqPlan best{1, (W + U - 1) / U};
   double best_eff = double(W) / (best.waves * U);
   for (int R = 2; R <= 64; ++R) {
     const int waves = (R * W + U - 1) / U;
-    if (waves > 16 || rq_shmem(R, waves, U, G, esize) > kMaxLds) break;
+    if (waves > 16 || rq_shmem(R, waves, U, G, esize, qb) > kMaxLds) break;
     const double eff = double(R * W) / (waves * U);
     if (eff > best_eff + 1e-9) {
       best = {R, waves};
@@ -593,15 +614,15 @@ int device_cus() {
   return n;
 }
 
-template <int G, typename TIn, int VEC>
-auto kernel_ptr() { return &rht_quant_kernel<G, TIn, VEC>; }
+template <int G, typename TIn, int VEC, int QB>
+auto kernel_ptr() { return &rht_quant_kernel<G, TIn, VEC, QB>; }
 
-template <int G, typename TIn, int VEC>
+template <int G, typename TIn, int VEC, int QB>
 hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp, uint8_t* q,
                     float* s, float* xrot, hipStream_t stream) {
   constexpr int L = Geo<G>::L, U = 64 / L;
   const int W = int(Kp / G);
-  RqPlan p = plan_rows(W, U, G, int(sizeof(TIn)));
+  RqPlan p = plan_rows(W, U, G, int(sizeof(TIn)), QB);
   // Byte offsets inside a block are 32-bit: keep R rows of stride ldx below 2 GiB.
   while (p.R > 1 && int64_t(p.R) * ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) {
     p.R = 1;
@@ -609,14 +630,14 @@ hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp,
   }
   if (p.waves > 16 || ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int nblocks = int((M + p.R - 1) / p.R);
-  const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)));
+  const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)), QB);
   if (shmem > kMaxLds) return hipErrorInvalidValue;
   if (shmem > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<G, TIn, VEC>()),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<G, TIn, VEC, QB>()),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
     if (e != hipSuccess) return e;
   }
-  auto kernel = rht_quant_kernel<G, TIn, VEC>;
+  auto kernel = rht_quant_kernel<G, TIn, VEC, QB>;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * p.waves, shmem) !=
           hipSuccess || per_cu < 1)
@@ -626,22 +647,29 @@ hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp,
                        x, int(M), int(K), long(ldx), int(Kp), W, p.R, nblocks, q, s, xrot);
 }
 
-template <typename TIn, int VEC>
-hipError_t launch_t(const TIn* x, int64_t M, int64_t K, int64_t ldx, int g, int64_t Kp,
-                    uint8_t* q, float* s, float* xrot, hipStream_t st) {
+template <typename TIn, int VEC, int QB>
+hipError_t launch_gq(const TIn* x, int64_t M, int64_t K, int64_t ldx, int g, int64_t Kp,
+                     uint8_t* q, float* s, float* xrot, hipStream_t st) {
   switch (g) {
-    case 16: return launch_g<16, TIn, VEC>(x, M, K, ldx, Kp, q, s, xrot, st);
-    case 64: return launch_g<64, TIn, VEC>(x, M, K, ldx, Kp, q, s, xrot, st);
-    case 256: return launch_g<256, TIn, VEC>(x, M, K, ldx, Kp, q, s, xrot, st);
-    case 1024: return launch_g<1024, TIn, VEC>(x, M, K, ldx, Kp, q, s, xrot, st);
+    case 16: return launch_g<16, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
+    case 64: return launch_g<64, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
+    case 256: return launch_g<256, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
+    case 1024: return launch_g<1024, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename TIn, int VEC>
+hipError_t launch_t(const TIn* x, int64_t M, int64_t K, int64_t ldx, int g, int64_t Kp,
+                    int qbits, uint8_t* q, float* s, float* xrot, hipStream_t st) {
+  if (qbits == 8) return launch_gq<TIn, VEC, 8>(x, M, K, ldx, g, Kp, q, s, xrot, st);
+  return launch_gq<TIn, VEC, 4>(x, M, K, ldx, g, Kp, q, s, xrot, st);
 }
 
 }  // namespace
 
 hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                               int g, int64_t Kp, int vec_bytes, uint8_t* q, float* s,
+                               int g, int64_t Kp, int qbits, int vec_bytes, uint8_t* q, float* s,
                                float* xrot, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (x_dtype == 1) {
@@ -650,17 +678,17 @@ hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K,
     if ((((M - 1) * ldx + K) & 1) != 0) vec_bytes = 2;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     switch (vec_bytes) {
-      case 16: return launch_t<uint16_t, 16>(xb, M, K, ldx, g, Kp, q, s, xrot, stream);
-      case 8: return launch_t<uint16_t, 8>(xb, M, K, ldx, g, Kp, q, s, xrot, stream);
-      case 4: return launch_t<uint16_t, 4>(xb, M, K, ldx, g, Kp, q, s, xrot, stream);
-      default: return launch_t<uint16_t, 2>(xb, M, K, ldx, g, Kp, q, s, xrot, stream);
+      case 16: return launch_t<uint16_t, 16>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
+      case 8: return launch_t<uint16_t, 8>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
+      case 4: return launch_t<uint16_t, 4>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
+      default: return launch_t<uint16_t, 2>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
     }
   }
   const float* xf = static_cast<const float*>(x);
   switch (vec_bytes) {
-    case 16: return launch_t<float, 16>(xf, M, K, ldx, g, Kp, q, s, xrot, stream);
-    case 8: return launch_t<float, 8>(xf, M, K, ldx, g, Kp, q, s, xrot, stream);
-    default: return launch_t<float, 4>(xf, M, K, ldx, g, Kp, q, s, xrot, stream);
+    case 16: return launch_t<float, 16>(xf, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
+    case 8: return launch_t<float, 8>(xf, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
+    default: return launch_t<float, 4>(xf, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
   }
 }
 

@@ -177,12 +177,12 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Large-tile kernel: 256 (m) x 256 (n) per workgroup, four waves of 128 x 128, each a 4 x 4
-// grid of v_mfma_i32_32x32x32_i8 blocks (the 32x32x32 form has twice the int8 throughput
-// of 16x16x64 on gfx950), K step of 128 codes.  Operands stream HBM -> LDS with buffer loads
-// straight into LDS (no VGPR staging, coalesced, rows past M or N and bytes past K' read as
-// zero) through a three-stage ring, so two K steps are in flight while one is multiplied.
-// The tile grid is walked in groups that keep each XCD's tiles in a compact block.
+// Large-tile kernel: 256 (m) x 256 (n) per workgroup of eight waves (two per SIMD), each a
+// 64 x 128 wave tile of 2 x 4 v_mfma_i32_32x32x32_i8 blocks (the 32x32x32 form has twice the
+// int8 throughput of 16x16x64 on gfx950).  K step: 64 bytes of codes per row (128 int4 or 64
+// int8 codes).  Operands stream HBM -> LDS with buffer loads straight into LDS (no VGPR
+// staging; rows past M or N and bytes past K' read as zero) through a four-stage ring.  The
+// tile grid is walked in groups that keep each XCD's tiles in a compact block.
 namespace big {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -190,10 +190,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-#ifndef CONVROT_GEMM_WAVES
-#define CONVROT_GEMM_WAVES 8
-#endif
-constexpr int kWaves = CONVROT_GEMM_WAVES;     // 4: one wave per SIMD; 8: two per SIMD
+constexpr int kWaves = 8;                      // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 256, kBN = 256;            // workgroup tile along m (activations) and n
 constexpr int kWavesN = 2, kWavesM = kWaves / kWavesN;
@@ -206,7 +203,6 @@ constexpr int kDmaA = kBM / 16, kDmaB = kBN / 16;  // 1 KB (16 rows x 64 B) tran
 constexpr int kDma = kDmaA + kDmaB;                // 32 per stage
 constexpr int kDmaPerWave = kDma / kWaves;
 constexpr uint32_t kOob = 0x80000000u;
-constexpr int kStages = 4;                         // LDS ring depth
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -254,62 +250,27 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t 
   }
 }
 
-// Wait for this wave's transfers of the stage needed next (see the K loop): those of the
-// kStages - 2 newest stages may stay in flight.  vmcnt(n) is 0x0F70 + n for n < 16 and
-// sets bits 15:14 to n >> 4 above that.
-__device__ __forceinline__ void wait_own_stage() {
-  constexpr int n = kDmaPerWave * (kStages - 2);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
-}
 
-// Packed fragments of one K step, as read from LDS.  For a 32-row block, lane l reads row
-// l % 32, chunks 2h and 2h + 1 (h = l / 32).  Weights and activations use the same mapping.
-struct Frags {
-  uint4 w[kGN][2], x[kGM][2];
-};
-
-__device__ __forceinline__ void read_frags(const uint8_t* st, int wn, int wm, int lane,
-                                           Frags& f) {
-  const int r32 = lane & 31, h = lane >> 5;
-  const uint4* A = reinterpret_cast<const uint4*>(st);
-  const uint4* B = reinterpret_cast<const uint4*>(st + kAStage);
-#pragma unroll
-  for (int i = 0; i < kGN; ++i) {
-    const int row = wn * kTN + 32 * i + r32;
-    f.w[i][0] = B[bswz(row, 2 * h)];
-    f.w[i][1] = B[bswz(row, 2 * h + 1)];
-  }
-#pragma unroll
-  for (int j = 0; j < kGM; ++j) {
-    const int row = wm * kTM + 32 * j + r32;
-    f.x[j][0] = A[bswz(row, 2 * h)];
-    f.x[j][1] = A[bswz(row, 2 * h + 1)];
-  }
-}
-
-// MFMA operand of substep s (32 codes): dwords 0-1 (s even) or 2-3 (s odd) of chunk s / 2,
-// each dword unpacked into its even and its odd codes.
-__device__ __forceinline__ v4i unpack_sub(const uint4 (&c)[2], int s) {
-  const uint32_t m = 0xF0F0F0F0u;
-  const uint4 v = c[s >> 1];
-  const uint32_t a = (s & 1) ? v.z : v.x, b = (s & 1) ? v.w : v.y;
-  return v4i{int((a << 4) & m), int(a & m), int((b << 4) & m), int(b & m)};
-}
-
-// One chunk (substeps 2c and 2c + 1) of every block's fragment.
+// Half of one K step's fragments: one 16-byte chunk per lane and 32-row block.  For a block,
+// lane l reads row l % 32 (h = l / 32).  int4: chunk 2h + c, i.e. codes 64h + 32c .. + 31,
+// feeding MFMA substeps 2c and 2c + 1; int8: chunk 2c + h, feeding substep c.  Weights and
+// activations use the same mapping, so the K order seen by the MFMA is the same on both
+// sides and the sums are unchanged.
 struct Half {
   uint4 w[kGN], x[kGM];
 };
 
+template <int QB>
 __device__ __forceinline__ void read_half(const uint8_t* st, int c, int wn, int wm, int lane,
                                           Half& f) {
   const int r32 = lane & 31, h = lane >> 5;
+  const int q = QB == 4 ? 2 * h + c : 2 * c + h;
   const uint4* A = reinterpret_cast<const uint4*>(st);
   const uint4* B = reinterpret_cast<const uint4*>(st + kAStage);
 #pragma unroll
-  for (int j = 0; j < kGM; ++j) f.x[j] = A[bswz(wm * kTM + 32 * j + r32, 2 * h + c)];
+  for (int j = 0; j < kGM; ++j) f.x[j] = A[bswz(wm * kTM + 32 * j + r32, q)];
 #pragma unroll
-  for (int i = 0; i < kGN; ++i) f.w[i] = B[bswz(wn * kTN + 32 * i + r32, 2 * h + c)];
+  for (int i = 0; i < kGN; ++i) f.w[i] = B[bswz(wn * kTN + 32 * i + r32, q)];
 }
 
 __device__ __forceinline__ v4i unpack_half(const uint4 v, int s) {
@@ -318,8 +279,18 @@ __device__ __forceinline__ v4i unpack_half(const uint4 v, int s) {
   return v4i{int((a << 4) & m), int(a & m), int((b << 4) & m), int(b & m)};
 }
 
-// The two substeps of one chunk.
+// The MFMA substeps of one chunk: two (int4, after unpacking) or one (int8, as loaded).
+template <int QB>
 __device__ __forceinline__ void mma_half(const Half& f, v16i (&acc)[kGN][kGM]) {
+  if constexpr (QB == 8) {
+#pragma unroll
+    for (int i = 0; i < kGN; ++i)
+#pragma unroll
+      for (int j = 0; j < kGM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            __builtin_bit_cast(v4i, f.w[i]), __builtin_bit_cast(v4i, f.x[j]), acc[i][j], 0, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     v4i w[kGN], x[kGM];
@@ -335,39 +306,6 @@ __device__ __forceinline__ void mma_half(const Half& f, v16i (&acc)[kGN][kGM]) {
   }
 }
 
-// The unpacking of substep s + 1 is interleaved with the matrix instructions of substep s:
-// one 32-cycle MFMA leaves room for several vector instructions, so the matrix pipe is not
-// left idle while operands are prepared (sched_group_barrier masks: 8 = MFMA, 2 = VALU).
-__device__ __forceinline__ void mma_frags(const Frags& f, v16i (&acc)[kGN][kGM]) {
-  v4i w[2][kGN], x[2][kGM];
-#pragma unroll
-  for (int i = 0; i < kGN; ++i) w[0][i] = unpack_sub(f.w[i], 0);
-#pragma unroll
-  for (int j = 0; j < kGM; ++j) x[0][j] = unpack_sub(f.x[j], 0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = s & 1;
-    if (s < 3) {
-#pragma unroll
-      for (int i = 0; i < kGN; ++i) w[c ^ 1][i] = unpack_sub(f.w[i], s + 1);
-#pragma unroll
-      for (int j = 0; j < kGM; ++j) x[c ^ 1][j] = unpack_sub(f.x[j], s + 1);
-    }
-#pragma unroll
-    for (int i = 0; i < kGN; ++i)
-#pragma unroll
-      for (int j = 0; j < kGM; ++j)
-        acc[i][j] =
-            __builtin_amdgcn_mfma_i32_32x32x32_i8(w[c][i], x[c][j], acc[i][j], 0, 0, 0);
-    constexpr int kValuPerMfma = (6 * (kGN + kGM) + kGN * kGM - 1) / (kGN * kGM);
-#pragma unroll
-    for (int q = 0; q < kGN * kGM; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
-    }
-  }
-}
-
 // Dequantization epilogue of one 256 x 256 tile.  32x32 accumulator layout: lane l holds
 // column m = l % 32 of a block and, in register r, row n = 8 (r / 4) + 4 (l / 32) + r % 4.
 //   1. The tile's 256 activation scales, weight scales and bias values (loaded into registers
@@ -378,7 +316,7 @@ __device__ __forceinline__ void mma_frags(const Frags& f, v16i (&acc)[kGN][kGM])
 //      nearest even by v_cvt_pk_bf16_f32) and writes them into the wave's own 32 x 128
 //      staging rows; the wave then reads the rows back and stores 16 contiguous bytes per
 //      lane, four whole 256-byte output rows per instruction.
-template <bool kDbg>
+template <bool kDbg, int QB>
 __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, uint8_t* st1,
                                          uint8_t* st2, uint8_t* st3, float xsv, float wsv,
                                          uint32_t bbits,
@@ -420,7 +358,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
         int32_t t[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          t[r] = acc[i][j][4 * g + r] >> 8;  // exact: products are multiples of 256
+          // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
+          t[r] = QB == 4 ? acc[i][j][4 * g + r] >> 8 : acc[i][j][4 * g + r];
           z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]), bv[r]);
         }
         if (kDbg && mrow + r32 < M) {  // raw integer sums, for verification only
@@ -462,8 +401,9 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
 }
 
 // kDbg: also store the raw integer sums (a separate instantiation keeps the production
-// kernel's register allocation free of the extra live values).
-template <bool kDbg>
+// kernel's register allocation free of the extra live values).  QB: code width, 4 (packed
+// int4, K'/2 bytes per row) or 8 (int8, K' bytes per row).
+template <bool kDbg, int QB>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
@@ -496,7 +436,7 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
   int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   asm volatile("" : "+s"(wave));
   const int wn = wave & 1, wm = wave >> 1;
-  const int rowB = Kp / 2;
+  const int rowB = Kp * QB / 8;  // bytes of codes per row
   const int nsteps = (rowB + kBKB - 1) / kBKB;
   // Epilogue factors, loaded now so their latency hides behind the K loop.
   float xsv, wsv;
@@ -518,39 +458,33 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
 #pragma unroll
     for (int j = 0; j < kGM; ++j) acc[i][j] = v16i{};
 
-  // The ring: stage k of the K loop lives in buffer k % 4, and the fragments of stage k + 1
-  // are read from LDS while the matrix cores work on stage k.  Transfers are issued for
-  // every step, also past the end (their offsets are then out of range and they write
-  // zeros that no step uses), so that every wait has the same form.  Ordering at the top of
-  // step k: each wave waits for its own transfers of stage k + 1 (vmcnt) and for its reads
-  // of stage k (lgkmcnt); a plain s_barrier then makes every wave's transfers visible and
-  // guarantees that no wave still reads buffer k % 4, which is refilled with stage k + 4.
-  // (A fenced __syncthreads would also drain the transfers still in flight.)  The loop is
-  // unrolled by four so every buffer is named statically, which lets the compiler keep the
-  // newer transfers in flight.
-#if CONVROT_GEMM_WAVES == 8
-  // Two waves per SIMD, 256 registers each: fragments are handled one chunk (two of the four
-  // MFMA substeps) at a time.  The first chunk of stage k + 1 is read during step k and the
-  // second chunk of stage k at the start of step k, so the matrix instructions never wait for
-  // LDS.  Step k waits for stage k + 1 (stage k + 2 may stay in flight), then a plain
-  // s_barrier makes every wave's transfers visible and guarantees that buffer (k - 1) % 4,
-  // refilled now with stage k + 3, is no longer read.
+  // The ring: stage k of the K loop lives in buffer k % 4.  Transfers are issued for every
+  // step, also past the end (their offsets are then out of range and they write zeros that
+  // no step uses), so that every wait has the same form.  Fragments are handled one chunk
+  // (half a step) at a time, 256 registers per wave: the first chunk of stage k + 1 is read
+  // during step k and the second chunk of stage k at the start of step k, so the matrix
+  // instructions do not wait for LDS.  Step k waits for this wave's transfers of stage k + 1
+  // (those of stage k + 2 may stay in flight) and for its LDS reads; a plain s_barrier then
+  // makes every wave's transfers visible and guarantees that buffer (k - 1) % 4, refilled now
+  // with stage k + 3, is no longer read.  (A fenced __syncthreads would also drain the newer
+  // transfers.)  The loop is unrolled by four so every buffer is named statically, which
+  // lets the compiler keep the newer transfers in flight.
   Half f0, f1, g0;
   issue_stage(st0, ra, rb, rowB, 0, wave, lane);
   issue_stage(st1, ra, rb, rowB, 1, wave, lane);
   issue_stage(st2, ra, rb, rowB, 2, wave, lane);
   __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerWave));  // vmcnt: stage 0 landed
   __builtin_amdgcn_s_barrier();
-  read_half(st0, 0, wn, wm, lane, f0);
+  read_half<QB>(st0, 0, wn, wm, lane, f0);
 #define CONVROT_STEP(K, CUR, NEXT, REFILL)                                          \
   __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerWave); /* vmcnt: stage K + 1 landed */  \
   __builtin_amdgcn_s_waitcnt(0xC07F);               /* lgkmcnt(0) */                \
   __builtin_amdgcn_s_barrier();                                                     \
   issue_stage(REFILL, ra, rb, rowB, (K) + 3, wave, lane);                           \
-  read_half(CUR, 1, wn, wm, lane, f1);                                              \
-  read_half(NEXT, 0, wn, wm, lane, g0);                                             \
-  mma_half(f0, acc);                                                                \
-  mma_half(f1, acc);                                                                \
+  read_half<QB>(CUR, 1, wn, wm, lane, f1);                                          \
+  read_half<QB>(NEXT, 0, wn, wm, lane, g0);                                         \
+  mma_half<QB>(f0, acc);                                                            \
+  mma_half<QB>(f1, acc);                                                            \
   f0 = g0;
   int k = 0;
   for (; k + 4 <= nsteps; k += 4) {
@@ -569,52 +503,32 @@ void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restric
     }
   }
 #undef CONVROT_STEP
-#else
-  Frags fa, fb;
-  issue_stage(st0, ra, rb, rowB, 0, wave, lane);
-  issue_stage(st1, ra, rb, rowB, 1, wave, lane);
-  issue_stage(st2, ra, rb, rowB, 2, wave, lane);
-  wait_own_stage();
-  __builtin_amdgcn_s_barrier();
-  issue_stage(st3, ra, rb, rowB, 3, wave, lane);
-  read_frags(st0, wn, wm, lane, fa);
-#define CONVROT_STEP(K, NEXT, REFILL, CUR, NXT)                                     \
-  wait_own_stage();                                                                 \
-  __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) */                              \
-  __builtin_amdgcn_s_barrier();                                                     \
-  issue_stage(REFILL, ra, rb, rowB, (K) + 4, wave, lane);                           \
-  read_frags(NEXT, wn, wm, lane, NXT);                                              \
-  __builtin_amdgcn_sched_barrier(0); /* reads first: they have a whole step to land */ \
-  mma_frags(CUR, acc);
-  int k = 0;
-  for (; k + 4 <= nsteps; k += 4) {
-    CONVROT_STEP(k, st1, st0, fa, fb)
-    CONVROT_STEP(k + 1, st2, st1, fb, fa)
-    CONVROT_STEP(k + 2, st3, st2, fa, fb)
-    CONVROT_STEP(k + 3, st0, st3, fb, fa)
-  }
-  if (k < nsteps) {
-    CONVROT_STEP(k, st1, st0, fa, fb)
-    if (k + 1 < nsteps) {
-      CONVROT_STEP(k + 1, st2, st1, fb, fa)
-      if (k + 2 < nsteps) {
-        CONVROT_STEP(k + 2, st3, st2, fa, fb)
-      }
-    }
-  }
-#undef CONVROT_STEP
-#endif
 
   // Epilogue, staged through LDS so that global stores are whole rows.  The last steps
   // issued zero-filling transfers after their final wait: drain them before the stage
   // buffers are reused.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __builtin_amdgcn_s_barrier();
-  epilogue<kDbg>(acc, st0, st1, st2, st3, xsv, wsv, bbits, M, N, m0, n0, wave, lane, y,
+  epilogue<kDbg, QB>(acc, st0, st1, st2, st3, xsv, wsv, bbits, M, N, m0, n0, wave, lane, y,
                  acc_dbg);
 }
 
 }  // namespace big
+
+template <int QB>
+hipError_t launch_big(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                      const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
+                      int32_t* acc_dbg, hipStream_t stream) {
+  const int tiles_m = int((M + big::kBM - 1) / big::kBM);
+  const int tiles_n = int((N + big::kBN - 1) / big::kBN);
+  const int T = tiles_m * tiles_n;
+  const dim3 grid(unsigned(8 * ((T + 7) / 8))), block(big::kThreads);
+  if (acc_dbg != nullptr)
+    return launch_kernel(big::w4a4_gemm_big_kernel<true, QB>, grid, block, 0, stream, xq, xs, wq,
+                         ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
+  return launch_kernel(big::w4a4_gemm_big_kernel<false, QB>, grid, block, 0, stream, xq, xs, wq,
+                       ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
+}
 
 }  // namespace
 
@@ -624,16 +538,8 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   // The large tile needs 16-byte packed rows and enough work to fill the chip.
-  if ((Kp / 2) % 16 == 0 && M * N >= (int64_t(1) << 21) && M >= big::kBM / 2) {
-    const int tiles_m = int((M + big::kBM - 1) / big::kBM), tiles_n = int((N + big::kBN - 1) / big::kBN);
-    const int T = tiles_m * tiles_n;
-    const dim3 grid(unsigned(8 * ((T + 7) / 8))), block(big::kThreads);
-    if (acc_dbg != nullptr)
-      return launch_kernel(big::w4a4_gemm_big_kernel<true>, grid, block, 0, stream, xq, xs, wq,
-                           ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
-    return launch_kernel(big::w4a4_gemm_big_kernel<false>, grid, block, 0, stream, xq, xs, wq, ws,
-                         bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
-  }
+  if ((Kp / 2) % 16 == 0 && M * N >= (int64_t(1) << 21) && M >= big::kBM / 2)
+    return launch_big<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   const dim3 grid(unsigned((M + kBM - 1) / kBM), unsigned((N + kBN - 1) / kBN));
   const dim3 block(256);
   if (vec_bytes == 16)
@@ -641,6 +547,13 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                          int(M), int(N), int(Kp), y, acc_dbg);
   return launch_kernel(w4a4_gemm_kernel<8>, grid, block, 0, stream, xq, xs, wq, ws, bias, int(M),
                        int(N), int(Kp), y, acc_dbg);
+}
+
+hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq,
+                            const float* ws, const uint16_t* bias, int64_t M, int64_t N,
+                            int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  return launch_big<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
 }
 
 }  // namespace convrot

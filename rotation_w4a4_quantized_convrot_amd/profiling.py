@@ -30,7 +30,7 @@ CALIBRATION_BYTES = 256 << 20          # bench.py --copy-calibration: bytes read
 
 # kernel key -> (substring of the demangled name, source file under csrc/)
 KERNELS = {
-    "w4a4_gemm_big_kernel": ("w4a4_gemm_big_kernel<false>", "w4a4_gemm.hip"),
+    "w4a4_gemm_big_kernel": ("w4a4_gemm_big_kernel<false, 4>", "w4a4_gemm.hip"),
     "rht_quant_kernel": ("rht_quant_kernel<256", "rht_quant.hip"),
 }
 

@@ -178,3 +178,48 @@ def test_python_binding_rejects_cpu_tensors(lib):
         cr.convrot_rotate_quant_act(torch.zeros((2, 16), dtype=torch.bfloat16), 16)
     with pytest.raises(ValueError, match="power of 4, got 8"):
         cr.convrot_rotate_quant_act(torch.zeros((2, 16), dtype=torch.bfloat16), 8)
+
+
+def test_w8a8_workspace_bytes(lib):
+    assert cr.convrot_w8a8_workspace_bytes(4608, 3072, 256) == 4608 * 3072 + 18432
+    assert cr.convrot_w8a8_workspace_bytes(3, 17, 16) == 256 + 256
+    assert cr.convrot_w8a8_workspace_bytes(10, 100, 8) == 0
+    assert cr.convrot_w8a8_workspace_bytes(-1, 100, 16) == 0
+
+
+def test_int8_entry_points_validate(lib):
+    E = _lib
+    rq = lambda **k: lib.convrot_rotate_quant_act_i8(  # noqa: E731
+        k.get("x", A16), k.get("dt", 1), k.get("M", 4), k.get("K", 64), k.get("ldx", k.get("K", 64)),
+        k.get("g", 16), k.get("q", A16), k.get("s", A16), k.get("rot"), None)
+    assert rq(g=8) == E.CONVROT_ERR_GROUP
+    assert rq(g=4096) == E.CONVROT_ERR_UNSUPPORTED
+    assert rq(dt=5) == E.CONVROT_ERR_DTYPE
+    assert rq(K=64, ldx=63) == E.CONVROT_ERR_SHAPE
+    # int8 codes take twice the register room: g = 1024 bf16 rows stop at K' = 53248
+    assert rq(K=53249, g=1024) == E.CONVROT_ERR_UNSUPPORTED
+    assert rq(K=32769, g=1024, dt=0) == E.CONVROT_ERR_UNSUPPORTED
+    assert rq(K=28673, g=1024, dt=0) == E.CONVROT_ERR_UNSUPPORTED
+    assert rq(K=30721, g=256, dt=0) == E.CONVROT_ERR_UNSUPPORTED
+    assert rq(K=30721, g=64, dt=0) == E.CONVROT_ERR_UNSUPPORTED
+    assert rq(q=None) == E.CONVROT_ERR_NULL
+    assert rq(q=A16 + 8) == E.CONVROT_ERR_ALIGN
+    assert rq(M=0, x=None, q=None, s=None) == E.CONVROT_OK
+    assert lib.convrot_quant_weight_i8(A16, 1, 4, 64, 32, A16, A16, None) == E.CONVROT_ERR_GROUP
+    gm = lambda **k: lib.convrot_w8a8_gemm(  # noqa: E731
+        k.get("xq", A16), A16, A16, A16, k.get("b"), k.get("M", 4), 4, k.get("Kp", 64),
+        k.get("y", A16), k.get("acc"), None)
+    assert gm(Kp=40) == E.CONVROT_ERR_SHAPE
+    assert gm(Kp=65536 + 16) == E.CONVROT_ERR_UNSUPPORTED
+    assert gm(xq=None) == E.CONVROT_ERR_NULL
+    assert gm(xq=A16 + 8) == E.CONVROT_ERR_ALIGN
+    assert gm(b=MIS) == E.CONVROT_ERR_ALIGN
+    assert gm(M=0, xq=None, y=None) == E.CONVROT_OK
+    ln = lambda **k: lib.convrot_w8a8_linear(  # noqa: E731
+        A16, 1, k.get("M", 4), 64, k.get("g", 16), A16, A16, 4, None, A16, k.get("wsp", A16 * 16),
+        k.get("nbytes", 1 << 20), None)
+    assert ln(g=32) == E.CONVROT_ERR_GROUP
+    assert ln(wsp=None) == E.CONVROT_ERR_NULL
+    assert ln(wsp=A16 * 16 + 16) == E.CONVROT_ERR_ALIGN
+    assert ln(nbytes=cr.convrot_w8a8_workspace_bytes(4, 64, 16) - 1) == E.CONVROT_ERR_WORKSPACE
+    assert ln(M=0, wsp=None) == E.CONVROT_OK

@@ -20,7 +20,7 @@ def _write(d, counter, rows):
                         "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": val})
 
 
-GEMM = "void convrot::(anonymous namespace)::big::w4a4_gemm_big_kernel<false>(...)"
+GEMM = "void convrot::(anonymous namespace)::big::w4a4_gemm_big_kernel<false, 4>(...)"
 CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<...>>"
 
 
