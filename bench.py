@@ -13,6 +13,9 @@ cores); the rotate+quantize kernel's HBM roofline is reported alongside.  Each k
 launch duration comes from HIP events on the launch stream around batches of back-to-back
 launches of that kernel.  The CPU oracle is timed over whole passes of the same layer
 (`cpu_baseline`).
+
+`--codes int8` measures the W8A8 variant the same way (convrot_rotate_quant_act_i8 and
+convrot_w8a8_gemm, the kernels convrot_w8a8_linear enqueues) and prints its own line.
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "W4A4 linear TOPS + rotate-quant GB/s (% of roofline) at M=4608,K=3072,g=256"
+METRIC_W8A8 = "W8A8 linear TOPS + rotate-quant GB/s (% of roofline) at M=4608,K=3072,g=256"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 matrix throughput (5.0 POP/s)
 MALL_BYTES = 256 << 20          # Infinity Cache; rotate inputs through > 2x this
@@ -38,6 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="attn_proj")
+    p.add_argument("--codes", choices=("int4", "int8"), default="int4",
+                   help="int4: the W4A4 layer (default); int8: the W8A8 variant")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = all)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -93,10 +99,12 @@ def gpu_bench(args, wl):
     w = torch.from_numpy(wkmod.weights(wl)).to(tdt).to(dev)
     b = wkmod.bias(wl)
     bias = None if b is None else torch.from_numpy(b).to(torch.bfloat16).to(dev)
-    wq, ws = cr.convrot_quant_weight(w, g)
+    i8 = args.codes == "int8"
+    qbytes = Kp if i8 else Kp // 2              # code bytes per row
+    wq, ws = (cr.convrot_quant_weight_i8 if i8 else cr.convrot_quant_weight)(w, g)
     n_y = 4
     ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(n_y)]
-    xq = torch.empty((M, Kp // 2), dtype=torch.uint8, device=dev)
+    xq = torch.empty((M, qbytes), dtype=torch.uint8, device=dev)
     xsc = torch.empty((M,), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
@@ -106,6 +114,8 @@ def gpu_bench(args, wl):
     y_ptrs = [t.data_ptr() for t in ys]
     b_ptr = None if bias is None else bias.data_ptr()
     rq, gemm = lib.convrot_rotate_quant_act, lib.convrot_w4a4_gemm
+    if i8:
+        rq, gemm = lib.convrot_rotate_quant_act_i8, lib.convrot_w8a8_gemm
     xq_p, xs_p, wq_p, ws_p = xq.data_ptr(), xsc.data_ptr(), wq.data_ptr(), ws.data_ptr()
 
     def step(i):
@@ -165,13 +175,13 @@ def gpu_bench(args, wl):
 
     ms_step = (t1 - t0) * 1e3 / K_steps
     ops = 2.0 * M * N * Kp
-    rq_bytes = M * K * x0.element_size() + M * Kp // 2 + 4 * M
+    rq_bytes = M * K * x0.element_size() + M * qbytes + 4 * M
     rq_us = float(np.mean(rq_ms) * 1e3)
     gemm_us = float(np.mean(gemm_ms) * 1e3)
     rq_gbps = rq_bytes / (rq_us * 1e-6) / 1e9
     gemm_tops = ops / (gemm_us * 1e-6) / 1e12
-    # GEMM algorithmic bytes: packed operands once, scales, bias, bf16 output
-    gemm_bytes = M * Kp // 2 + N * Kp // 2 + 4 * (M + N) + (2 * N if bias is not None else 0) + 2 * M * N
+    # GEMM algorithmic bytes: code operands once, scales, bias, bf16 output
+    gemm_bytes = M * qbytes + N * qbytes + 4 * (M + N) + (2 * N if bias is not None else 0) + 2 * M * N
     return {
         "ms_per_step": ms_step, "ms_per_step_events": step_ms_events,
         "value": ops / (ms_step * 1e-3) / 1e12,
@@ -193,13 +203,15 @@ def cpu_baseline(args, wl):
     x = wkmod.activations(wl)
     w = wkmod.weights(wl)
     b = wkmod.bias(wl)
-    refw = O.quantize_weight(w, wl.g)               # offline path, not timed
+    i8 = args.codes == "int8"
+    refw = (O.quantize_weight_int8 if i8 else O.quantize_weight)(w, wl.g)   # offline, untimed
     rows = args.cpu_rows or wl.M
     xs = x[:rows]
     passes, t0 = 0, time.perf_counter()
     while True:
-        r = O.rotate_quantize(xs, wl.g)
-        O.w4a4_linear_from_codes(r["codes"], r["scale"], refw["codes"], refw["scale"], b)
+        r = (O.rotate_quantize_int8 if i8 else O.rotate_quantize)(xs, wl.g)
+        lin = O.w8a8_linear_from_codes if i8 else O.w4a4_linear_from_codes
+        lin(r["codes"], r["scale"], refw["codes"], refw["scale"], b)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= args.cpu_seconds or passes >= 100:
@@ -225,12 +237,15 @@ def main():
     r = gpu_bench(args, wl)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl)
     from rotation_w4a4_quantized_convrot_amd import profiling
-    big = (wl.Kp // 2) % 16 == 0 and wl.M * wl.N >= (1 << 21) and wl.M >= 128
-    gemm_kernel = "w4a4_gemm_big_kernel" if big else "w4a4_gemm_kernel"
-    tg = profiling.read_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.txt"), gemm_kernel) \
-        if big else None
-    tq = profiling.read_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.txt"),
-                                "rht_quant_kernel") if wl.g == 256 else None
+    i8 = args.codes == "int8"
+    # the int4 GEMM takes its tiled MFMA kernel for large shapes with 16-byte packed rows
+    big = i8 or ((wl.Kp // 2) % 16 == 0 and wl.M * wl.N >= (1 << 21) and wl.M >= 128)
+    gemm_kernel = ("w8a8_gemm" if i8 else "w4a4_gemm") if big else "w4a4_gemm_kernel"
+    rq_kernel = "rht_quant_i8" if i8 else "rht_quant_i4"
+    traffic_file = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    tg = profiling.read_traffic(traffic_file, gemm_kernel) if big else None
+    plain = wl.g == 256 and wl.x_dtype == "bf16" and wl.K % 8 == 0
+    tq = profiling.read_traffic(traffic_file, rq_kernel) if plain else None
     roof = {"bound": "mfma", "achieved": r["gemm_tops"], "peak": INT8_PEAK_TOPS,
             "unit": "TFLOP/s", "frac": r["gemm_tops"] / INT8_PEAK_TOPS,
             "traffic": None if tg is None else tg["fetch_bytes"] + tg["write_bytes"],
@@ -240,10 +255,10 @@ def main():
     roof_rq = {"bound": "hbm", "achieved": r["rq_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                "frac": r["rq_gbps"] / HBM_PEAK_GBPS,
                "traffic": None if tq is None else tq["fetch_bytes"] + tq["write_bytes"],
-               "kernel": "rht_quant_kernel", "launch_us": r["rq_us"],
+               "kernel": rq_kernel, "launch_us": r["rq_us"],
                "algorithmic_bytes_per_launch": r["rq_bytes"]}
     out = {
-        "metric": METRIC, "value": r["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_W8A8 if i8 else METRIC, "value": r["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "g": wl.g, "Kp": wl.Kp,

@@ -406,11 +406,11 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
 template <bool kDbg, int QB>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
-void w4a4_gemm_big_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
-                          const uint8_t* __restrict__ wq, const float* __restrict__ ws,
-                          const uint16_t* __restrict__ bias, int M, int N, int Kp,
-                          int tiles_m, int tiles_n, uint16_t* __restrict__ y,
-                          int32_t* __restrict__ acc_dbg) {
+void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                       const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+                       const uint16_t* __restrict__ bias, int M, int N, int Kp,
+                       int tiles_m, int tiles_n, uint16_t* __restrict__ y,
+                       int32_t* __restrict__ acc_dbg) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[kStage], st1[kStage], st2[kStage],
       st3[kStage];
 
@@ -524,9 +524,9 @@ hipError_t launch_big(const uint8_t* xq, const float* xs, const uint8_t* wq, con
   const int T = tiles_m * tiles_n;
   const dim3 grid(unsigned(8 * ((T + 7) / 8))), block(big::kThreads);
   if (acc_dbg != nullptr)
-    return launch_kernel(big::w4a4_gemm_big_kernel<true, QB>, grid, block, 0, stream, xq, xs, wq,
+    return launch_kernel(big::quant_gemm_kernel<true, QB>, grid, block, 0, stream, xq, xs, wq,
                          ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
-  return launch_kernel(big::w4a4_gemm_big_kernel<false, QB>, grid, block, 0, stream, xq, xs, wq,
+  return launch_kernel(big::quant_gemm_kernel<false, QB>, grid, block, 0, stream, xq, xs, wq,
                        ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
 }
 

@@ -30,8 +30,10 @@ CALIBRATION_BYTES = 256 << 20          # bench.py --copy-calibration: bytes read
 
 # kernel key -> (substring of the demangled name, source file under csrc/)
 KERNELS = {
-    "w4a4_gemm_big_kernel": ("w4a4_gemm_big_kernel<false, 4>", "w4a4_gemm.hip"),
-    "rht_quant_kernel": ("rht_quant_kernel<256", "rht_quant.hip"),
+    "w4a4_gemm": ("quant_gemm_kernel<false, 4>", "w4a4_gemm.hip"),
+    "w8a8_gemm": ("quant_gemm_kernel<false, 8>", "w4a4_gemm.hip"),
+    "rht_quant_i4": ("rht_quant_kernel<256, unsigned short, 16, 4>", "rht_quant.hip"),
+    "rht_quant_i8": ("rht_quant_kernel<256, unsigned short, 16, 8>", "rht_quant.hip"),
 }
 
 
@@ -71,7 +73,14 @@ def calibration_kib(rows: List[dict]) -> float:
     return statistics.median(float(r["Counter_Value"]) for r in cand if int(r["Grid_Size"]) == g)
 
 
-def traffic(fetch_dir: str, write_dir: str) -> Dict[str, dict]:
+def traffic(fetch_dir, write_dir) -> Dict[str, dict]:
+    """Per-launch HBM bytes of each known kernel.  fetch_dir / write_dir may be lists of
+    paired runs (say one per code width); each pair is calibrated by its own copy kernel."""
+    if not isinstance(fetch_dir, str):
+        out = {}
+        for f, w in zip(fetch_dir, write_dir):
+            out.update(traffic(f, w))
+        return out
     fr, wr = _rows(_counter_file(fetch_dir)), _rows(_counter_file(write_dir))
     f_cal, w_cal = calibration_kib(fr), calibration_kib(wr)
     f_scale = CALIBRATION_BYTES / (f_cal * 1024.0)
@@ -154,8 +163,8 @@ def main(argv=None) -> int:
     tt.add_argument("csv")
     tt.add_argument("--last", type=int, required=True)
     t = sub.add_parser("traffic")
-    t.add_argument("--fetch", required=True)
-    t.add_argument("--write", required=True)
+    t.add_argument("--fetch", required=True, nargs="+")
+    t.add_argument("--write", required=True, nargs="+")
     t.add_argument("--out", required=True)
     t.add_argument("--command", default="")
     a = p.parse_args(argv)

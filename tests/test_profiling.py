@@ -20,7 +20,7 @@ def _write(d, counter, rows):
                         "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": val})
 
 
-GEMM = "void convrot::(anonymous namespace)::big::w4a4_gemm_big_kernel<false, 4>(...)"
+GEMM = "void convrot::(anonymous namespace)::big::quant_gemm_kernel<false, 4>(...)"
 CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<...>>"
 
 
@@ -32,19 +32,19 @@ def test_traffic_scaling_and_staleness(tmp_path):
     _write(tmp_path / "w", "WRITE_SIZE", [(GEMM, 55296, 50.0), (GEMM, 55296, 50.0),
                                           (CAL, 262144, 262144.0)])
     t = P.traffic(str(tmp_path / "f"), str(tmp_path / "w"))
-    g = t["w4a4_gemm_big_kernel"]
+    g = t["w4a4_gemm"]
     assert g["fetch_scale"] == pytest.approx(2.0) and g["write_scale"] == pytest.approx(1.0)
     assert g["fetch_bytes"] == pytest.approx(100.0 * 1024 * 2)    # first (cold) dispatch left out
     assert g["write_bytes"] == pytest.approx(50.0 * 1024)
     out = tmp_path / "traffic.txt"
     P.write_traffic(str(out), t, "cmd")
-    r = P.read_traffic(str(out), "w4a4_gemm_big_kernel")
+    r = P.read_traffic(str(out), "w4a4_gemm")
     assert r == {"fetch_bytes": pytest.approx(204800.0), "write_bytes": pytest.approx(51200.0)}
     # a different source hash means the kernel changed since: no traffic figure
     text = out.read_text().replace(g["source_sha256"], "0" * 64)
     out.write_text(text)
-    assert P.read_traffic(str(out), "w4a4_gemm_big_kernel") is None
-    assert P.read_traffic(str(tmp_path / "missing.txt"), "w4a4_gemm_big_kernel") is None
+    assert P.read_traffic(str(out), "w4a4_gemm") is None
+    assert P.read_traffic(str(tmp_path / "missing.txt"), "w4a4_gemm") is None
 
 
 def test_calibration_required(tmp_path):
