@@ -309,13 +309,51 @@ __device__ __forceinline__ void mma_half(const Half& f, v16i (&acc)[kGN][kGM]) {
 // Dequantization epilogue of one 256 x 256 tile.  32x32 accumulator layout: lane l holds
 // column m = l % 32 of a block and, in register r, row n = 8 (r / 4) + 4 (l / 32) + r % 4.
 //   1. The tile's 256 activation scales, weight scales and bias values (loaded into registers
-//      at kernel start, one of each per thread) are staged in LDS; each lane then keeps the
-//      factors of its 64 columns in registers.  A missing bias is -0.0, which leaves every
-//      sum unchanged in round-to-nearest-even, so the add needs no branch.
+//      at kernel start, one of each per thread; the bias widened to fp32) are staged in LDS.
+//      A missing bias is -0.0, which leaves every sum unchanged in round-to-nearest-even, so
+//      the add needs no branch.
 //   2. Per 32-row block of m, each lane converts its 4 x 16 accumulators (bf16 rounding to
 //      nearest even by v_cvt_pk_bf16_f32) and writes them into the wave's own 32 x 128
 //      staging rows; the wave then reads the rows back and stores 16 contiguous bytes per
 //      lane, four whole 256-byte output rows per instruction.
+template <bool kDbg, int QB>
+__device__ __forceinline__ void epi_block(const v16i (&acc)[kGN][kGM], int j, float sxm,
+                                          const float* fw, const float* fb, uint8_t* stage,
+                                          int M, int N, long mrow, long n0, int wn, int lane,
+                                          int32_t* __restrict__ acc_dbg) {
+  constexpr int kPitch = 272;  // bytes per staging row: 256 + 16 keeps rows 16-byte aligned
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < kGN; ++i) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * i + 8 * g + 4 * h;  // column within the wave's 128
+      const float4 w4 = *reinterpret_cast<const float4*>(fw + wn * kTN + c);
+      const float4 b4 = *reinterpret_cast<const float4*>(fb + wn * kTN + c);
+      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+      const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+      float z[4];
+      int32_t t[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
+        t[r] = QB == 4 ? acc[i][j][4 * g + r] >> 8 : acc[i][j][4 * g + r];
+        z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]), bv[r]);
+      }
+      if (kDbg && mrow + r32 < M) {  // raw integer sums, for verification only
+        const long n = n0 + wn * kTN + c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) acc_dbg[(mrow + r32) * (long)N + n + r] = t[r];
+      }
+      const bf16x2 lo = __builtin_convertvector((f32x2){z[0], z[1]}, bf16x2);
+      const bf16x2 hi = __builtin_convertvector((f32x2){z[2], z[3]}, bf16x2);
+      *reinterpret_cast<uint2*>(stage + r32 * kPitch + 2 * c) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
+  }
+}
+
 template <bool kDbg, int QB>
 __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, uint8_t* st1,
                                          uint8_t* st2, uint8_t* st3, float xsv, float wsv,
@@ -323,20 +361,20 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
                                          int M, int N, long m0, long n0, int wave, int lane,
                                          uint16_t* __restrict__ y,
                                          int32_t* __restrict__ acc_dbg) {
-  constexpr int kPitch = 272;  // bytes per staging row: 256 + 16 keeps rows 16-byte aligned
+  constexpr int kPitch = 272;
   float* fx = reinterpret_cast<float*>(st3);
   float* fw = fx + kBM;
-  uint16_t* fb = reinterpret_cast<uint16_t*>(fw + kBN);
+  float* fb = fw + kBN;
   const int tid = wave * 64 + lane;
   if (tid < kBM) {  // kBM == kBN
     fx[tid] = xsv;
     fw[tid] = wsv;
-    fb[tid] = uint16_t(bbits);
+    fb[tid] = __uint_as_float(bbits << 16);  // bf16 -> fp32 is exact
   }
   __syncthreads();
 
   const int wn = wave & 1, wm = wave >> 1;
-  const int r32 = lane & 31, h = lane >> 5;
+  const int r32 = lane & 31;
   // Each wave's 32 x 128 staging rows: three per stage buffer (st3 holds the factors).
   uint8_t* stage = (wave < 3 ? st0 : wave < 6 ? st1 : st2) + (wave % 3) * (32 * kPitch);
   const bool vec16 = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
@@ -344,36 +382,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
   for (int j = 0; j < kGM; ++j) {
     const long mrow = m0 + wm * kTM + 32 * j;  // first output row of this block
     const float sxm = fx[wm * kTM + 32 * j + r32];
-#pragma unroll
-    for (int i = 0; i < kGN; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = 32 * i + 8 * g + 4 * h;  // column within the wave's 128
-        const float4 w4 = *reinterpret_cast<const float4*>(fw + wn * kTN + c);
-        const uint2 b4 = *reinterpret_cast<const uint2*>(fb + wn * kTN + c);
-        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-        const float bv[4] = {__uint_as_float(b4.x << 16), __uint_as_float(b4.x & 0xFFFF0000u),
-                             __uint_as_float(b4.y << 16), __uint_as_float(b4.y & 0xFFFF0000u)};
-        float z[4];
-        int32_t t[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
-          t[r] = QB == 4 ? acc[i][j][4 * g + r] >> 8 : acc[i][j][4 * g + r];
-          z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]), bv[r]);
-        }
-        if (kDbg && mrow + r32 < M) {  // raw integer sums, for verification only
-          const long n = n0 + wn * kTN + c;
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n + r < N) acc_dbg[(mrow + r32) * (long)N + n + r] = t[r];
-        }
-        const bf16x2 lo = __builtin_convertvector((f32x2){z[0], z[1]}, bf16x2);
-        const bf16x2 hi = __builtin_convertvector((f32x2){z[2], z[3]}, bf16x2);
-        *reinterpret_cast<uint2*>(stage + r32 * kPitch + 2 * c) =
-            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-      }
-    }
+    epi_block<kDbg, QB>(acc, j, sxm, fw, fb, stage, M, N, mrow, n0, wn, lane, acc_dbg);
     // Same wave, in-order LDS: the rows written above are complete for the reads below.
     __builtin_amdgcn_wave_barrier();
     const int c16 = lane & 15;

@@ -203,6 +203,23 @@ def test_gemm_parity_full_range_codes(cr, M, N, Kp, with_bias):
     assert np.array_equal(y2.view(torch.int16).cpu().numpy().view(np.uint16), ref["out_bits"])
 
 
+@pytest.mark.parametrize("M,N,Kp", [(300, 500, 320), (4608, 3072, 256)])
+def test_gemm_extreme_scales(cr, M, N, Kp):
+    """Bit-exact outputs for scales down to the subnormal range and up to overflow."""
+    _announce(f"gemm extreme scales M={M} N={N} Kp={Kp}")
+    qx = wk.random_codes(M, Kp, seed=11)
+    qw = wk.random_codes(N, Kp, seed=12)
+    sx, sw = wk.extreme_scales(M, 13), wk.extreme_scales(N, 14)
+    b = wk.round_to_dtype(np.random.default_rng(15).standard_normal(N).astype(np.float32), "bf16")
+    ref = O.w4a4_linear_from_codes(qx, sx, qw, sw, b)
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(DEV)  # noqa: E731
+    y = cr.convrot_w4a4_gemm(dev(O.pack_int4(qx), torch.uint8), dev(sx, torch.float32),
+                             dev(O.pack_int4(qw), torch.uint8), dev(sw, torch.float32),
+                             dev(b, torch.float32).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref["out_bits"])
+
+
 LINEAR_CASES = [
     # M, K, N, g, dtype, bias
     (64, 256, 256, 16, "f32", False),       # the tiny fp32 workload's shape

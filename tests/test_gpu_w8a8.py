@@ -145,6 +145,23 @@ def test_w8a8_gemm_full_range(cr, M, N, Kp, with_bias):
     assert np.array_equal(y2.view(torch.int16).cpu().numpy().view(np.uint16), ref["out_bits"])
 
 
+def test_w8a8_gemm_extreme_scales(cr):
+    """Bit-exact outputs for scales down to the subnormal range and up to overflow."""
+    M, N, Kp = 300, 500, 320
+    _announce(f"w8a8 gemm extreme scales M={M} N={N} Kp={Kp}")
+    rng = np.random.default_rng(21)
+    qx = rng.integers(-128, 128, size=(M, Kp)).astype(np.int8)
+    qw = rng.integers(-128, 128, size=(N, Kp)).astype(np.int8)
+    sx, sw = wk.extreme_scales(M, 23), wk.extreme_scales(N, 24)
+    b = wk.round_to_dtype(rng.standard_normal(N).astype(np.float32), "bf16")
+    ref = O.w8a8_linear_from_codes(qx, sx, qw, sw, b)
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(DEV)  # noqa: E731
+    y = cr.convrot_w8a8_gemm(dev(qx, torch.int8), dev(sx, torch.float32), dev(qw, torch.int8),
+                             dev(sw, torch.float32), dev(b, torch.float32).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref["out_bits"])
+
+
 LINEAR_CASES = [
     # M, K, N, g, dtype, bias
     (64, 256, 256, 16, "f32", False), (200, 3072, 320, 256, "bf16", True),

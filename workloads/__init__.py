@@ -167,3 +167,21 @@ def random_scales(n: int, seed: int) -> np.ndarray:
     """Positive float32 scales spanning a few binades, for GEMM-only tests."""
     rng = np.random.default_rng(seed)
     return (rng.uniform(0.5, 2.0, size=n) * np.exp2(rng.integers(-6, 2, size=n))).astype(np.float32)
+
+
+def extreme_scales(n: int, seed: int) -> np.ndarray:
+    """fp32 scales over the whole range the dequantization must handle bit-exactly: zero,
+    values so small that the products are subnormal or vanish, huge values, negatives, and
+    ordinary ones, interleaved so that some 32-row blocks are all ordinary."""
+    rng = np.random.default_rng(seed)
+    mant = rng.uniform(1.0, 2.0, size=n)
+    kind = rng.integers(0, 6, size=n)
+    expo = np.select([kind == 0, kind == 1, kind == 2, kind == 3],
+                     [rng.integers(-149, -110, size=n), rng.integers(-127, -117, size=n),
+                      rng.integers(90, 100, size=n), rng.integers(-8, 2, size=n)],
+                     rng.integers(-8, 2, size=n))
+    s = (mant * np.exp2(expo.astype(np.float64))).astype(np.float32)
+    s[kind == 4] *= -1
+    s[rng.random(n) < 0.05] = 0.0
+    s[:64] = (rng.uniform(0.5, 2.0, size=min(n, 64)) * 2.0 ** -5).astype(np.float32)
+    return s
