@@ -524,6 +524,216 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
 
 }  // namespace big
 
+// ---------------------------------------------------------------------------------------
+// Skinny kernel, for few activation rows (decode-like M, or too few 256 x 256 tiles to fill
+// the chip): a workgroup owns 32 output columns (weight rows) x 32 MB activation rows and
+// splits the K steps between its 16 / MB waves.  Operands go straight from global memory
+// into MFMA registers (each weight byte is read from HBM once; the activation codes, shared
+// by every workgroup, come from L2) through a ring of kDepth K steps in flight per wave, and
+// the partial sums meet in LDS (64 KB).  The dequantization factors are fetched before the
+// K loop so that their latency overlaps it.  The chunk-to-lane mapping and the int4
+// unpacking are those of the tiled kernel.
+namespace skinny {
+
+using big::v16i;
+using big::f32x2;
+using big::bf16x2;
+constexpr int kTN = 32;      // output columns (weight rows) per workgroup
+constexpr int kStepB = 64;   // bytes of codes per row per K step
+
+template <int MB>
+struct Shape {
+  static constexpr int kWaves = 16 / MB, kThreads = 64 * kWaves;
+  static constexpr int kDepth = MB == 4 ? 2 : 4;          // K steps in flight per wave
+  static constexpr int kGroups = (MB * 256 + kThreads - 1) / kThreads;  // outputs / 4 / thread
+};
+
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int row, int byte, int rowB) {
+  const uint32_t off = byte < rowB ? uint32_t(row * rowB + byte) : big::kOob;
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// One K step of this lane's operands: chunks c = 0, 1 of its weight row and of its row in
+// each 32-row activation block.
+template <int MB>
+struct Frag {
+  uint4 w[2], x[MB][2];
+};
+
+template <int QB, int MB>
+__device__ __forceinline__ void load_step(Frag<MB>& f, __amdgpu_buffer_rsrc_t rw,
+                                          __amdgpu_buffer_rsrc_t rx, int step, int rowB,
+                                          int lane) {
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int q = QB == 4 ? 2 * h + c : 2 * c + h;
+    const int byte = step * kStepB + 16 * q;
+    f.w[c] = ld16(rw, r32, byte, rowB);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) f.x[j][c] = ld16(rx, 32 * j + r32, byte, rowB);
+  }
+}
+
+template <int QB, int MB>
+__device__ __forceinline__ void mma_step(const Frag<MB>& f, v16i (&acc)[MB]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if constexpr (QB == 8) {
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, f.w[c]),
+                                                       __builtin_bit_cast(v4i, f.x[j][c]),
+                                                       acc[j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const v4i w = big::unpack_half(f.w[c], s);
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+          acc[j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w, big::unpack_half(f.x[j][c], s),
+                                                         acc[j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <bool kDbg, int QB, int MB>
+__global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
+    const float* __restrict__ ws, const uint16_t* __restrict__ bias, int M, int N, int Kp,
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg) {
+  constexpr int kWaves = Shape<MB>::kWaves, kThreads = Shape<MB>::kThreads;
+  constexpr int kDepth = Shape<MB>::kDepth, kGroups = Shape<MB>::kGroups;
+  __shared__ int32_t red[kWaves * MB * 16 * 64];  // 64 KB: every wave's partial sums
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long n0 = (long)blockIdx.x * kTN, m0 = (long)blockIdx.y * (32 * MB);
+  const int rowB = Kp * QB / 8;  // bytes of codes per row
+  // Rows past the tile (or past N, M) read as zero through the buffer range check.
+  const __amdgpu_buffer_rsrc_t rw = big::rsrc(wq + n0 * rowB, min(long(N) - n0, long(kTN)) * rowB);
+  const __amdgpu_buffer_rsrc_t rx =
+      big::rsrc(xq + m0 * rowB, min(long(M) - m0, long(32 * MB)) * rowB);
+  const int nsteps = (rowB + kStepB - 1) / kStepB;
+  const int per = (nsteps + kWaves - 1) / kWaves;
+  const int k0 = min(nsteps, wave * per), k1 = min(nsteps, k0 + per);
+
+  v16i acc[MB];
+#pragma unroll
+  for (int j = 0; j < MB; ++j) acc[j] = v16i{};
+  Frag<MB> f[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (k0 + d < k1) load_step<QB, MB>(f[d], rw, rx, k0 + d, rowB, lane);
+
+  // Dequantization factors of this thread's output groups (four consecutive columns of one
+  // row each; see below), fetched now so that the loads overlap the K loop.
+  float fsx[kGroups], fw[kGroups][4], fb[kGroups][4];
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) {
+    const int gi = tid + kThreads * i;
+    const int l = gi & 63, g = (gi >> 6) & 3, j = gi >> 8;
+    const long m = m0 + 32 * j + (l & 31), n = n0 + 8 * g + 4 * (l >> 5);
+    const bool live = gi < MB * 256 && m < M;
+    fsx[i] = live ? xs[m] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool in = live && n + r < N;
+      fw[i][r] = in ? ws[n + r] : 0.f;
+      // bf16 -> fp32 is exact; a missing bias is -0.0, an exact identity for the add
+      fb[i][r] = (in && bias != nullptr) ? __uint_as_float(uint32_t(bias[n + r]) << 16) : -0.0f;
+    }
+  }
+
+  for (int k = k0; k < k1; k += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      if (k + d < k1) {
+        mma_step<QB, MB>(f[d], acc);
+        if (k + d + kDepth < k1) load_step<QB, MB>(f[d], rw, rx, k + d + kDepth, rowB, lane);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < MB; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[((wave * MB + j) * 16 + r) * 64 + lane] = acc[j][r];
+  __syncthreads();
+
+  // Final sums and dequantization, four consecutive columns per thread.  32x32 accumulator
+  // layout: lane l holds row m = l % 32 of a block and, in register r, column
+  // n = 8 (r / 4) + 4 (l / 32) + r % 4.
+  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+#pragma unroll
+  for (int i = 0; i < kGroups; ++i) {
+    const int gi = tid + kThreads * i;
+    const int l = gi & 63, g = (gi >> 6) & 3, j = gi >> 8;
+    const long m = m0 + 32 * j + (l & 31);
+    const long n = n0 + 8 * g + 4 * (l >> 5);
+    if (gi >= MB * 256 || m >= M || n >= N) continue;
+    float z[4];
+    int32_t t[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int32_t a = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) a += red[((w * MB + j) * 16 + 4 * g + r) * 64 + l];
+      // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
+      t[r] = QB == 4 ? a >> 8 : a;
+      z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], fsx[i]), fw[i][r]), fb[i][r]);
+    }
+    const bf16x2 lo = __builtin_convertvector((f32x2){z[0], z[1]}, bf16x2);
+    const bf16x2 hi = __builtin_convertvector((f32x2){z[2], z[3]}, bf16x2);
+    uint16_t* yp = y + m * (long)N + n;
+    if (vec) {
+      *reinterpret_cast<uint2*>(yp) =
+          make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    } else {
+      const uint16_t o[4] = {uint16_t(__builtin_bit_cast(uint32_t, lo)),
+                             uint16_t(__builtin_bit_cast(uint32_t, lo) >> 16),
+                             uint16_t(__builtin_bit_cast(uint32_t, hi)),
+                             uint16_t(__builtin_bit_cast(uint32_t, hi) >> 16)};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) yp[r] = o[r];
+    }
+    if (kDbg) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) acc_dbg[m * (long)N + n + r] = t[r];
+    }
+  }
+}
+
+}  // namespace skinny
+
+template <int QB, int MB>
+hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* wq,
+                            const float* ws, const uint16_t* bias, int64_t M, int64_t N,
+                            int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
+  const dim3 grid(unsigned((N + skinny::kTN - 1) / skinny::kTN), unsigned((M + 32 * MB - 1) / (32 * MB)));
+  const dim3 block(skinny::Shape<MB>::kThreads);
+  if (acc_dbg != nullptr)
+    return launch_kernel(skinny::quant_gemm_skinny_kernel<true, QB, MB>, grid, block, 0, stream,
+                         xq, xs, wq, ws, bias, int(M), int(N), int(Kp), y, acc_dbg);
+  return launch_kernel(skinny::quant_gemm_skinny_kernel<false, QB, MB>, grid, block, 0, stream, xq,
+                       xs, wq, ws, bias, int(M), int(N), int(Kp), y, acc_dbg);
+}
+
+// Largest M routed to the skinny kernel, per code width.
+constexpr int64_t kSkinnyMaxM4 = 512, kSkinnyMaxM8 = 256;
+
+// Activation rows per skinny workgroup: 32, 64 or 128.
+template <int QB>
+hipError_t launch_skinny(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                         const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
+                         int32_t* acc_dbg, hipStream_t stream) {
+  if (M <= 32) return launch_skinny_mb<QB, 1>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+  if (M <= 64) return launch_skinny_mb<QB, 2>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+  return launch_skinny_mb<QB, 4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+}
+
 template <int QB>
 hipError_t launch_big(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                       const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
@@ -546,8 +756,17 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, int vec_bytes,
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+  const bool rows16 = (Kp / 2) % 16 == 0;  // 16-byte packed rows
+#ifdef CONVROT_GEMM_PATH
+  if (CONVROT_GEMM_PATH == 1 && rows16)
+    return launch_skinny<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+#endif
+  // Few activation rows: 256 x 256 tiles would leave most CUs idle (measured on MI355X at
+  // N = 3072: the skinny kernel is faster up to M = 512).
+  if (rows16 && M <= kSkinnyMaxM4)
+    return launch_skinny<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   // The large tile needs 16-byte packed rows and enough work to fill the chip.
-  if ((Kp / 2) % 16 == 0 && M * N >= (int64_t(1) << 21) && M >= big::kBM / 2)
+  if (rows16 && M * N >= (int64_t(1) << 21) && M >= big::kBM / 2)
     return launch_big<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   const dim3 grid(unsigned((M + kBM - 1) / kBM), unsigned((N + kBN - 1) / kBN));
   const dim3 block(256);
@@ -562,6 +781,13 @@ hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             const float* ws, const uint16_t* bias, int64_t M, int64_t N,
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
+#ifdef CONVROT_GEMM_PATH
+  if (CONVROT_GEMM_PATH == 1)
+    return launch_skinny<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+#endif
+  // int8 operands double the skinny kernel's bytes per MFMA: it wins up to M = 256.
+  if (M <= kSkinnyMaxM8)
+    return launch_skinny<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   return launch_big<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
 }
 

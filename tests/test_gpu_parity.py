@@ -169,11 +169,14 @@ def test_empty_inputs(cr):
 
 GEMM_CASES = [
     # M, N, Kp, bias
-    (1, 1, 16, False), (17, 5, 48, True), (128, 128, 128, False), (200, 136, 1024, True),
-    (129, 130, 256, True), (300, 257, 3072, False), (64, 256, 3328, True), (33, 96, 12288, False),
+    # K'/2 not a multiple of 16: the 128 x 128 kernel
+    (1, 1, 16, False), (17, 5, 48, True), (700, 300, 1040, True),
+    # M <= 512: the skinny kernel (32, 64 and 128-row workgroups, ragged M, N and K)
+    (1, 40, 128, True), (128, 128, 128, False), (200, 136, 1024, True), (129, 130, 256, True),
+    (300, 257, 3072, False), (64, 256, 3328, True), (33, 96, 12288, False),
+    (300, 7000, 3328, False), (512, 3072, 3072, True),
     # large-tile kernel (M N >= 2^21): ragged M and N, several tiles, K tails
     (600, 3500, 512, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
-    (300, 7000, 3328, False),
 ]
 
 
@@ -267,7 +270,7 @@ def test_convlinear4bit_module(cr):
 
 # Full-size workloads in the launch configuration the benchmark times; the oracle checks a
 # sample of rows (rows are independent) including every outlier row it picks.
-FULL = ["rotate_quant", "attn_proj", "mlp_down", "proj_out", "proj_out_padded"]
+FULL = ["rotate_quant", "attn_proj", "mlp_down", "proj_out", "proj_out_padded", "few_tokens"]
 
 
 @pytest.mark.slow

@@ -32,3 +32,4 @@ def test_full_workload_table():
     assert t["mlp_down"].Kp == 12288 and t["mlp_down"].n_out_rows == 23
     assert t["proj_out"].n_out_rows == 92
     assert t["proj_out_padded"].Kp == 3328
+    assert (t["few_tokens"].M, t["few_tokens"].N, t["few_tokens"].n_out_rows) == (64, 3072, 1)

@@ -87,6 +87,10 @@ WORKLOADS = {
         n_out_rows=_pct_rows(9216, 0.01), row_scale=50.0, n_out_cols=8, col_scale=30.0,
         w_std=0.01,
         description="single-stream proj_out batch 2, X[9216x15360] W[3072x15360], g=1024"),
+    "few_tokens": Workload(
+        "few_tokens", M=64, K=3072, N=3072, g=256, x_dtype="bf16",
+        n_out_rows=1, row_scale=50.0, n_out_cols=8, col_scale=30.0, w_std=0.02, bias_std=0.01,
+        description="few tokens (m <= 128), attention-projection weights, X[64x3072] + bias"),
     "proj_out_padded": Workload(
         "proj_out_padded", M=4608, K=3100, N=3072, g=256, x_dtype="bf16",
         n_out_rows=_pct_rows(4608, 0.01), row_scale=50.0, n_out_cols=8, col_scale=30.0,
