@@ -358,8 +358,10 @@ __device__ __forceinline__ float candidate_slack() {
 // prefetching block b + gridDim.x into registers while block b is processed.  One workgroup
 // barrier per block: per-row maxima meet in LDS through atomics on four rotating buffers;
 // the row scale (which needs the exact maximum) is stored one iteration later.
-template <int G, typename TIn, int VEC, int QB>
-__global__ __launch_bounds__(1024) void rht_quant_kernel(const TIn* __restrict__ x, int M, int K,
+// MW: most waves per workgroup (launch bound 64 MW).  g = 1024 holds 64 values per lane and
+// needs the registers of 8-wave workgroups; rows too long for 8 waves take MW = 16.
+template <int G, typename TIn, int VEC, int QB, int MW>
+__global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restrict__ x, int M, int K,
                                                          long ldx, int Kp, int W, int R,
                                                          int nblocks, uint8_t* __restrict__ q,
                                                          float* __restrict__ s,
@@ -587,12 +589,12 @@ size_t rq_shmem(int R, int waves, int U, int G, int esize, int qb) {
          size_t(waves) * U * G * esize;
 }
 
-RqPlan plan_rows(int W, int U, int G, int esize, int qb) {
+RqPlan plan_rows(int W, int U, int G, int esize, int qb, int max_waves) {
   RqPlan best{1, (W + U - 1) / U};
   double best_eff = double(W) / (best.waves * U);
   for (int R = 2; R <= 64; ++R) {
     const int waves = (R * W + U - 1) / U;
-    if (waves > 16 || rq_shmem(R, waves, U, G, esize, qb) > kMaxLds) break;
+    if (waves > max_waves || rq_shmem(R, waves, U, G, esize, qb) > kMaxLds) break;
     const double eff = double(R * W) / (waves * U);
     if (eff > best_eff + 1e-9) {
       best = {R, waves};
@@ -614,30 +616,26 @@ int device_cus() {
   return n;
 }
 
-template <int G, typename TIn, int VEC, int QB>
-auto kernel_ptr() { return &rht_quant_kernel<G, TIn, VEC, QB>; }
-
-template <int G, typename TIn, int VEC, int QB>
-hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp, uint8_t* q,
-                    float* s, float* xrot, hipStream_t stream) {
+template <int G, typename TIn, int VEC, int QB, int MW>
+hipError_t launch_plan(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp, RqPlan p,
+                       uint8_t* q, float* s, float* xrot, hipStream_t stream) {
   constexpr int L = Geo<G>::L, U = 64 / L;
   const int W = int(Kp / G);
-  RqPlan p = plan_rows(W, U, G, int(sizeof(TIn)), QB);
   // Byte offsets inside a block are 32-bit: keep R rows of stride ldx below 2 GiB.
   while (p.R > 1 && int64_t(p.R) * ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) {
     p.R = 1;
     p.waves = (W + U - 1) / U;
   }
-  if (p.waves > 16 || ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (p.waves > MW || ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int nblocks = int((M + p.R - 1) / p.R);
   const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)), QB);
   if (shmem > kMaxLds) return hipErrorInvalidValue;
+  auto kernel = rht_quant_kernel<G, TIn, VEC, QB, MW>;
   if (shmem > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<G, TIn, VEC, QB>()),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
     if (e != hipSuccess) return e;
   }
-  auto kernel = rht_quant_kernel<G, TIn, VEC, QB>;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * p.waves, shmem) !=
           hipSuccess || per_cu < 1)
@@ -645,6 +643,21 @@ hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp,
   const int grid = int(std::min<int64_t>(nblocks, int64_t(device_cus()) * per_cu));
   return launch_kernel(kernel, dim3(unsigned(grid)), dim3(unsigned(64 * p.waves)), shmem, stream,
                        x, int(M), int(K), long(ldx), int(Kp), W, p.R, nblocks, q, s, xrot);
+}
+
+template <int G, typename TIn, int VEC, int QB>
+hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp, uint8_t* q,
+                    float* s, float* xrot, hipStream_t stream) {
+  constexpr int L = Geo<G>::L, U = 64 / L;
+  const int W = int(Kp / G);
+  const int es = int(sizeof(TIn));
+  if constexpr (G == 1024) {
+    const RqPlan p8 = plan_rows(W, U, G, es, QB, 8);
+    if (p8.waves <= 8)
+      return launch_plan<G, TIn, VEC, QB, 8>(x, M, K, ldx, Kp, p8, q, s, xrot, stream);
+  }
+  return launch_plan<G, TIn, VEC, QB, 16>(x, M, K, ldx, Kp, plan_rows(W, U, G, es, QB, 16), q, s,
+                                          xrot, stream);
 }
 
 template <typename TIn, int VEC, int QB>
