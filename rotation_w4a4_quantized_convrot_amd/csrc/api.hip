@@ -38,10 +38,11 @@ int elem_size(int32_t dtype) { return dtype == CONVROT_F32 ? 4 : dtype == CONVRO
 
 // Widest power-of-two vector width (<= 16 bytes) that divides both the base address and
 // the row stride in bytes.
+// Bytes per input load of the rotate+quantize kernel.  Buffer loads need dword-aligned
+// addresses only, so every row whose elements all start on 4-byte boundaries takes 16-byte
+// loads; otherwise (bf16 rows at an odd element offset) 2-byte loads.
 int vector_width(const void* x, int64_t ld_bytes) {
-  int v = 16;
-  while (v > 1 && (!aligned(x, (size_t)v) || (ld_bytes % v) != 0)) v /= 2;
-  return v;
+  return aligned(x, 4) && (ld_bytes % 4) == 0 ? 16 : 2;
 }
 
 int check_group(int64_t g) {

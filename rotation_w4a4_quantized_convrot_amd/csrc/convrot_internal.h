@@ -9,8 +9,8 @@ namespace convrot {
 // Launches the fused pad + group-wise RHT + per-row absmax + quantize + pack kernel on rows
 // [0, M) of x (row stride ldx elements).  g in {16, 64, 256, 1024}; Kp = K' <= 65536.
 // x_dtype: 0 = fp32, 1 = bf16.  qbits: 4 (int4 codes, K'/2 bytes per row, scale = max/7) or
-// 8 (int8 codes, K' bytes per row, scale = max/127).  vec_bytes: widest aligned vector load
-// (2, 4, 8 or 16 bytes).
+// 8 (int8 codes, K' bytes per row, scale = max/127).  vec_bytes: bytes per input load, 16
+// (every element dword aligned) or 2 (bf16 rows at odd element offsets).
 hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                                int g, int64_t Kp, int qbits, int vec_bytes, uint8_t* q, float* s,
                                float* xrot, hipStream_t stream);

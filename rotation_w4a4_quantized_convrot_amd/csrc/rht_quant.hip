@@ -690,19 +690,13 @@ hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K,
     // the first byte past x, wide loads would drop it, so read element by element.
     if ((((M - 1) * ldx + K) & 1) != 0) vec_bytes = 2;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
-    switch (vec_bytes) {
-      case 16: return launch_t<uint16_t, 16>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-      case 8: return launch_t<uint16_t, 8>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-      case 4: return launch_t<uint16_t, 4>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-      default: return launch_t<uint16_t, 2>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-    }
+    if (vec_bytes == 16)
+      return launch_t<uint16_t, 16>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
+    return launch_t<uint16_t, 2>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
   }
-  const float* xf = static_cast<const float*>(x);
-  switch (vec_bytes) {
-    case 16: return launch_t<float, 16>(xf, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-    case 8: return launch_t<float, 8>(xf, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-    default: return launch_t<float, 4>(xf, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-  }
+  // fp32 elements are dword aligned: always 16-byte loads
+  return launch_t<float, 16>(static_cast<const float*>(x), M, K, ldx, g, Kp, qbits, q, s, xrot,
+                             stream);
 }
 
 }  // namespace convrot
