@@ -189,3 +189,22 @@ def extreme_scales(n: int, seed: int) -> np.ndarray:
     s[rng.random(n) < 0.05] = 0.0
     s[:64] = (rng.uniform(0.5, 2.0, size=min(n, 64)) * 2.0 ** -5).astype(np.float32)
     return s
+
+
+def offset_row_outliers(M: int, K: int, n_rows: int, offset: float, n_cols: int = 8,
+                        col_scale: float = 30.0, seed: int = SEED_X,
+                        dtype: str = "bf16") -> np.ndarray:
+    """X [M x K] ~ N(0, 1) whose first ``n_rows`` rows of a permutation carry a common
+    same-sign offset across every channel (a whole-token outlier that a global rotation
+    accumulates), plus ``n_cols`` channel outliers scaled by ``col_scale``; rounded once to
+    ``dtype``."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    pick = np.random.default_rng(SEED_PICK)
+    rows = pick.permutation(M)[:n_rows]
+    cols = pick.permutation(K)[:n_cols]
+    if len(rows):
+        x[rows, :] += np.float32(offset)
+    if len(cols):
+        x[:, cols] *= np.float32(col_scale)
+    return round_to_dtype(x, dtype)
