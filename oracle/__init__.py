@@ -12,4 +12,7 @@ from .convrot_oracle import (  # noqa: F401
     w4a4_linear_from_codes, zero_pad_columns,
     INT8_QMAX, INT8_QMIN, rotate_quantize_int8, quantize_weight_int8, w8a8_linear_from_codes,
     convlinear8bit,
+    MX_BLOCK, E2M1_EMAX, E8M0_BIAS, E2M1_GRID, e2m1_decode, e2m1_encode, mx_block_exponents,
+    quantize_mxfp4, mxfp4_values, rotate_quantize_mxfp4, quantize_weight_mxfp4,
+    mxfp4_linear_from_codes, convlinear_fp4,
 )

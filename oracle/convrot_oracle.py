@@ -282,6 +282,108 @@ def convlinear8bit(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], g: 
     return {"x": xr, "w": wr, **lin}
 
 
+# --------------------------------------------------------------------------
+# Floating-point 4-bit ConvRot.  [AUTHOR] says the method also suits floating-point
+# quantization but fixes no format.  Reading: MXFP4 as the OCP Microscaling (MX)
+# Specification v1.0 defines it (a published standard, not one of the pages): blocks of 32
+# consecutive rotated values along K share an E8M0 scale 2^(floor(log2(block absmax)) - 2),
+# 2 being the exponent of E2M1's largest normal value (6 = 1.5 * 2^2); each value becomes
+# the E2M1 number nearest to value / scale, ties to the even mantissa, magnitudes beyond 6
+# clamped to 6.  Same rotation, same row layouts as int4 (two codes per byte), plus one
+# E8M0 byte per block.
+# --------------------------------------------------------------------------
+MX_BLOCK = 32
+E2M1_EMAX = 2
+E8M0_BIAS = 127
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of 4-bit E2M1 codes: bit 3 sign, bits 2-1 exponent (bias 1), bit 0 mantissa;
+    exponent 0 is subnormal (0 or 0.5)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.exp2(e - 1.0) * (1.0 + 0.5 * m))
+    return np.where(c & 8, -mag, mag)
+
+
+E2M1_GRID = e2m1_decode(np.arange(8))  # 0, 0.5, 1, 1.5, 2, 3, 4, 6
+
+
+def e2m1_encode(t: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code to t (exact float64 input), ties to the even code, so that
+    magnitudes above 6 saturate at 6; the sign bit follows t's sign (-0.0 -> code 8)."""
+    t = np.asarray(t, dtype=np.float64)
+    a = np.abs(t)
+    d = np.abs(a[..., None] - E2M1_GRID)  # distance to each of the 8 magnitudes
+    dmin = d.min(axis=-1, keepdims=True)
+    tied = d == dmin
+    idx = np.argmax(tied & (np.arange(8) % 2 == 0), axis=-1)  # an even code, if one is nearest
+    has_even = np.any(tied & (np.arange(8) % 2 == 0), axis=-1)
+    idx = np.where(has_even, idx, np.argmax(tied, axis=-1))
+    return (idx | np.where(np.signbit(t), 8, 0)).astype(np.uint8)
+
+
+def mx_block_exponents(yf: np.ndarray) -> np.ndarray:
+    """Shared exponent of every 32-value block of each row: floor(log2(absmax)) - 2, clamped
+    to E8M0's range [-127, 127]; an all-zero block takes -127."""
+    yf = np.asarray(yf, dtype=np.float64)
+    rows, n = yf.shape
+    if n % MX_BLOCK:
+        raise ValueError("row length must be a multiple of 32")
+    amax = np.max(np.abs(yf.reshape(rows, n // MX_BLOCK, MX_BLOCK)), axis=2)
+    _, ex = np.frexp(amax)  # amax = mant * 2^ex, mant in [0.5, 1): floor(log2) = ex - 1
+    e = np.where(amax > 0, ex.astype(np.int64) - 1 - E2M1_EMAX, -E8M0_BIAS)
+    return np.clip(e, -E8M0_BIAS, E8M0_BIAS)
+
+
+def quantize_mxfp4(yf: np.ndarray):
+    """(E2M1 codes [rows, n] as nibbles, E8M0 bytes [rows, n / 32])."""
+    yf = np.asarray(yf, dtype=np.float64)
+    e = mx_block_exponents(yf)
+    scale = np.repeat(np.exp2(e.astype(np.float64)), MX_BLOCK, axis=1)
+    return e2m1_encode(yf / scale), (e + E8M0_BIAS).astype(np.uint8)
+
+
+def mxfp4_values(codes: np.ndarray, e8m0: np.ndarray) -> np.ndarray:
+    """Decoded values: E2M1 value * 2^(E8M0 - 127) of its block (float64, exact)."""
+    s = np.exp2(np.asarray(e8m0, dtype=np.float64) - E8M0_BIAS)
+    return e2m1_decode(codes) * np.repeat(s, MX_BLOCK, axis=1)
+
+
+def rotate_quantize_mxfp4(a: np.ndarray, g: int) -> dict:
+    """Pad, rotate, round to fp32, MXFP4-quantize every 32-value block, pack."""
+    yf = to_f32(rotate_groups(a, g))
+    codes, e8m0 = quantize_mxfp4(yf)
+    return {"yf": yf, "codes": codes, "scales": e8m0, "packed": pack_int4(codes)}
+
+
+def quantize_weight_mxfp4(w: np.ndarray, g: int) -> dict:
+    """Offline MXFP4 weight path (blocks along K of each output channel)."""
+    return rotate_quantize_mxfp4(w, g)
+
+
+def mxfp4_linear_from_codes(cx, ex, cw, ew, bias=None) -> dict:
+    """sum_k x_k w_k of the decoded values in float64 (every product is exact; the sum is exact
+    unless a row's block scales span more than ~45 binades), the same with magnitudes (for
+    accumulation error bounds), and bf16(fp32(fp32(sum) + bias)) as bits."""
+    vx, vw = mxfp4_values(cx, ex), mxfp4_values(cw, ew)
+    z = vx @ vw.T
+    mag = np.abs(vx) @ np.abs(vw).T
+    zf = z.astype(np.float32)
+    if bias is not None:
+        zf = (zf + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    return {"sum": z, "abs_sum": mag, "out_bits": f32_to_bf16_bits(zf)}
+
+
+def convlinear_fp4(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], g: int) -> dict:
+    """The MXFP4 forward pass: the same rotation, MXFP4 codes on both sides."""
+    xr = rotate_quantize_mxfp4(x, g)
+    wr = quantize_weight_mxfp4(w, g)
+    lin = mxfp4_linear_from_codes(xr["codes"], xr["scales"], wr["codes"], wr["scales"], bias)
+    return {"x": xr, "w": wr, **lin}
+
+
 def reference_linear_fp64(x, w, bias=None) -> np.ndarray:
     """Unquantized X W^T + b in float64 (report-only error reference; parity unpinned)."""
     y = np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T

@@ -497,4 +497,123 @@ def pin_int8_end_to_end_closed_form(o):
         assert abs(float(z) - K * c * d) <= 1e-5 * abs(K * c * d)
 
 
+# ------------------------------------------------- MXFP4 (OCP Microscaling v1.0)
+def _rne_e2m1_by_binade(a: float) -> float:
+    """Independent E2M1 rounding of a magnitude: one mantissa bit above 1 (steps of 2^(e-1) in
+    [2^e, 2^(e+1))), steps of 0.5 below 1, Python's round() for ties to even, clamp at 6."""
+    if a < 1.0:
+        r = round(2.0 * a) / 2.0
+    else:
+        e = math.floor(math.log2(a))
+        step = 2.0 ** (e - 1)
+        r = round(a / step) * step
+    return min(r, 6.0)
+
+
+def pin_e2m1_format(o):
+    """E2M1: eight magnitudes 0 < 0.5 < 1 < ... < 6 (largest normal 1.5 * 2^2, smallest
+    subnormal 0.5), codes 8-15 the negatives, and every magnitude encodes back to its code."""
+    v = o.e2m1_decode(np.arange(16))
+    assert np.all(np.diff(v[:8]) > 0) and v[0] == 0.0
+    assert v[7] == 1.5 * 2 ** 2 and v[1] == 0.5 and v[2] == 1.0
+    assert np.array_equal(v[8:], -v[:8])
+    assert np.array_equal(o.e2m1_encode(v[:8]), np.arange(8))
+    assert np.array_equal(o.e2m1_encode(-v[1:8]), np.arange(9, 16))
+    assert o.e2m1_encode(np.array([-0.0]))[0] == 8 and o.e2m1_encode(np.array([0.0]))[0] == 0
+
+
+def pin_e2m1_rounding(o):
+    """Nearest value with ties to the even mantissa and saturation at 6, against an
+    independent per-binade rounding (Python's round) on random and tie inputs."""
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0]
+    assert list(o.e2m1_decode(o.e2m1_encode(np.array(ties)))) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0,
+                                                                  4.0, 6.0]
+    rng = np.random.default_rng(30)
+    a = np.concatenate([rng.uniform(0, 8, 2000), rng.uniform(0, 100, 200), np.array(ties)])
+    got = o.e2m1_decode(o.e2m1_encode(a))
+    want = np.array([_rne_e2m1_by_binade(float(t)) for t in a])
+    assert np.array_equal(got, want)
+    assert np.array_equal(o.e2m1_decode(o.e2m1_encode(-a)), -want)
+
+
+def pin_mx_block_scale(o):
+    """The shared exponent puts every nonzero block's absmax / scale in [4, 8): the block
+    maximum always encodes to 4 or 6; an all-zero block takes 2^-127; scaling a block by 2^j
+    shifts its exponent by j and leaves its codes alone."""
+    rng = np.random.default_rng(31)
+    y = rng.standard_normal((5, 256)) * np.exp2(rng.integers(-20, 20, size=(5, 1)))
+    y[2, 32:64] = 0.0
+    e = o.mx_block_exponents(y)
+    blocks = np.abs(y.reshape(5, 8, 32)).max(axis=2)
+    live = blocks > 0
+    ratio = blocks[live] / np.exp2(e[live].astype(np.float64))
+    assert np.all((ratio >= 4) & (ratio < 8))
+    assert e[2, 1] == -127
+    codes, e8 = o.quantize_mxfp4(y)
+    top = np.abs(o.e2m1_decode(codes)).reshape(5, 8, 32).max(axis=2)
+    assert np.all(np.isin(top[live], [4.0, 6.0]))
+    codes2, e82 = o.quantize_mxfp4(y * 2.0 ** 7)
+    assert np.array_equal(codes2, codes) and np.array_equal(e82[live], e8[live] + 7)
+    assert np.array_equal(e8, (e + 127).astype(np.uint8))
+
+
+def pin_mxfp4_round_trip(o):
+    """Blocks of E2M1 values times 2^j whose largest magnitude is 4 or 6 come back exactly."""
+    rng = np.random.default_rng(32)
+    vals = o.e2m1_decode(rng.integers(0, 16, size=(4, 128)))
+    vals[:, ::32] = rng.choice([4.0, -4.0, 6.0, -6.0], size=(4, 4))
+    j = rng.integers(-30, 30, size=(4, 4))
+    y = vals * np.repeat(np.exp2(j.astype(np.float64)), 32, axis=1)
+    codes, e8 = o.quantize_mxfp4(y)
+    assert np.array_equal(o.mxfp4_values(codes, e8), y)
+    assert np.array_equal(e8.astype(np.int64), j + 127)
+
+
+def pin_mxfp4_gemm_brute_force(o):
+    """The float64 sum of decoded products equals exact rational arithmetic (fractions)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(33)
+    for M, N, K in ((3, 2, 64), (2, 3, 32)):
+        cx = rng.integers(0, 16, size=(M, K)).astype(np.uint8)
+        cw = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+        ex = rng.integers(120, 136, size=(M, K // 32)).astype(np.uint8)
+        ew = rng.integers(120, 136, size=(N, K // 32)).astype(np.uint8)
+        r = o.mxfp4_linear_from_codes(cx, ex, cw, ew)
+        vx = [[Fraction(float(o.e2m1_decode(np.array([cx[m, k]]))[0])) *
+               Fraction(2) ** (int(ex[m, k // 32]) - 127) for k in range(K)] for m in range(M)]
+        vw = [[Fraction(float(o.e2m1_decode(np.array([cw[n, k]]))[0])) *
+               Fraction(2) ** (int(ew[n, k // 32]) - 127) for k in range(K)] for n in range(N)]
+        for m in range(M):
+            for n in range(N):
+                exact = sum(a * b for a, b in zip(vx[m], vw[n]))
+                assert Fraction(float(r["sum"][m, n])) == exact
+                assert Fraction(float(r["abs_sum"][m, n])) == sum(abs(a * b) for a, b in zip(vx[m], vw[n]))
+    # block scales spanning ~100 binades: float64 rounding, far below any kernel tolerance
+    cx = rng.integers(0, 16, size=(1, 64)).astype(np.uint8)
+    ex = np.array([[80, 180]], dtype=np.uint8)
+    r = o.mxfp4_linear_from_codes(cx, ex, cx, ex)
+    vx = [Fraction(float(o.e2m1_decode(np.array([cx[0, k]]))[0])) *
+          Fraction(2) ** (int(ex[0, k // 32]) - 127) for k in range(64)]
+    exact = sum(a * a for a in vx)
+    assert abs(Fraction(float(r["sum"][0, 0])) - exact) <= Fraction(2) ** -50 * exact
+
+
+def pin_mxfp4_end_to_end_closed_form(o):
+    """Constant rows c = 6 * 2^i and d = 4 * 2^j: the regular rotation keeps them constant,
+    every code is 6 resp. 4 with block scale 2^i resp. 2^j, and out = bf16(K' c d + b)."""
+    import torch
+    for g, K, i, j in ((64, 128, 0, -3), (256, 512, -2, 1), (1024, 1024, 3, -5)):
+        c, d = 6.0 * 2.0 ** i, -4.0 * 2.0 ** j
+        x = np.full((2, K), c)
+        w = np.full((3, K), d)
+        b = np.array([0.5, -1.0, 0.0], dtype=np.float32)
+        r = o.convlinear_fp4(x, w, b, g)
+        assert np.all(o.e2m1_decode(r["x"]["codes"]) == 6.0)
+        assert np.all(o.e2m1_decode(r["w"]["codes"]) == -4.0)
+        assert np.all(r["x"]["scales"] == 127 + i) and np.all(r["w"]["scales"] == 127 + j)
+        assert np.all(r["sum"] == K * c * d)
+        want = torch.tensor(np.float32(K * c * d) + b, dtype=torch.float32).to(torch.bfloat16)
+        assert np.array_equal(r["out_bits"], np.tile(want.view(torch.int16).numpy().view(np.uint16), (2, 1)))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

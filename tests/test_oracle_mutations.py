@@ -110,6 +110,20 @@ def _rotate_quantize_int8_scale7(a, g):
     return {"yf": r["yf"], "scale": s, "codes": _orig["quantize"](r["yf"], s, 127, -128)}
 
 
+def _e2m1_ties_away(t):
+    # nearest magnitude, ties to the larger one
+    t = np.asarray(t, dtype=np.float64)
+    a = np.abs(t)
+    d = np.abs(a[..., None] - O.E2M1_GRID)
+    idx = 7 - np.argmin(d[..., ::-1], axis=-1)
+    return (idx | np.where(np.signbit(t), 8, 0)).astype(np.uint8)
+
+
+def _e2m1_no_negative_zero(t):
+    c = _orig["e2m1_encode"](t)
+    return np.where(c == 8, 0, c).astype(np.uint8)
+
+
 MUTATIONS = {
     "sylvester_base": ({"base_regular_hadamard": _sylvester_base}, ["pin_regular"]),
     "negated_base": ({"base_regular_hadamard": lambda: -_orig["base_regular_hadamard"]()},
@@ -132,6 +146,10 @@ MUTATIONS = {
     "int8_qmax_128": ({"INT8_QMAX": 128}, ["pin_int8_round_trip", "pin_int8_rotate_quantize"]),
     "int8_int4_scale": ({"rotate_quantize_int8": _rotate_quantize_int8_scale7},
                         ["pin_int8_rotate_quantize", "pin_int8_end_to_end_closed_form"]),
+    "e2m1_ties_away": ({"e2m1_encode": _e2m1_ties_away}, ["pin_e2m1_rounding"]),
+    "e2m1_lost_sign_of_zero": ({"e2m1_encode": _e2m1_no_negative_zero}, ["pin_e2m1_format"]),
+    "mx_emax_3": ({"E2M1_EMAX": 3}, ["pin_mx_block_scale", "pin_mxfp4_round_trip",
+                                     "pin_mxfp4_end_to_end_closed_form"]),
 }
 
 
