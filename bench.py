@@ -225,8 +225,19 @@ def cpu_baseline(args, wl):
         if dt >= args.cpu_seconds or passes >= 100:
             break
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    blas = sorted({p.get("internal_api", "?") for p in threadpoolctl.threadpool_info()})
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     ops = 2.0 * rows * wl.N * wl.Kp * passes
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "cpu_model": model, "blas": ",".join(blas),
             "sample": f"{passes} passes of the layer on {rows} of {wl.M} rows, all {wl.N} "
                       f"outputs (rotate+quantize, int GEMM, dequant; {dt:.1f} s)",
             "seconds": dt}
@@ -271,12 +282,14 @@ def main():
     roof.update({"frac": roof["achieved"] / roof["peak"],
                  "traffic": None if tg is None else tg["fetch_bytes"] + tg["write_bytes"],
                  "kernel": gemm_kernel, "launch_us": r["gemm_us"],
+                 "launch_us_median": r["gemm_us_median"],
                  "algorithmic_ops_per_launch": r["gemm_ops"],
                  "algorithmic_bytes_per_launch": r["gemm_bytes"]})
     roof_rq = {"bound": "hbm", "achieved": r["rq_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                "frac": r["rq_gbps"] / HBM_PEAK_GBPS,
                "traffic": None if tq is None else tq["fetch_bytes"] + tq["write_bytes"],
                "kernel": rq_kernel, "launch_us": r["rq_us"],
+               "launch_us_median": r["rq_us_median"],
                "algorithmic_bytes_per_launch": r["rq_bytes"]}
     out = {
         "metric": METRIC_W8A8 if i8 else METRIC, "value": r["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
