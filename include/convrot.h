@@ -196,6 +196,34 @@ CONVROT_API int convrot_w8a8_linear(const void* x, int32_t x_dtype, int64_t M, i
                         const int8_t* wq, const float* ws, int64_t N, const void* bias,
                         void* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Floating-point 4-bit variant (MXFP4).  [AUTHOR]: ConvRot also suits floating-point
+ * quantization; the pages fix no format, and this library reads it as MXFP4 of the OCP
+ * Microscaling (MX) Specification v1.0, the format gfx950's scaled FP4 matrix instructions
+ * take.  The same group-wise regular rotation, then every 32 consecutive rotated values of
+ * a row share one E8M0 scale byte e = floor(log2(absmax)) - 2 + 127 (clamped to >= 0; an
+ * all-zero block takes 0), and each value becomes the E2M1 code nearest to value / 2^(e-127),
+ * ties to the even mantissa, magnitudes beyond 6 saturating at 6, the sign bit following the
+ * value (-0.0 -> 0x8).  Codes: two per byte, value 2j in the low nibble, row stride K'/2
+ * bytes; scales: row stride K'/32 bytes.  The block maxima are those of the fp32 rotation:
+ * a block's exponent may differ from the definition's only where its maximum lies within
+ * the rotation's rounding error of a power of two, and a code only at a rounding tie.
+ * g must be 64, 256 or 1024 (g = 16: UNSUPPORTED).
+ * --------------------------------------------------------------------------------------- */
+
+/* Online activation path, MXFP4: as convrot_rotate_quant_act, with
+ *   xq   device, uint8 [M][K'/2] E2M1 codes, 16-byte aligned;
+ *   xbs  device, uint8 [M][K'/32] E8M0 block scales (no alignment).
+ * K' limits as for int4 codes.  M = 0 is a no-op.
+ * Errors: GROUP, UNSUPPORTED, SHAPE, NULL, DTYPE, ALIGN, HIP. */
+CONVROT_API int convrot_rotate_quant_act_mxfp4(const void* x, int32_t x_dtype, int64_t M,
+                                               int64_t K, int64_t ldx, int64_t g, uint8_t* xq,
+                                               uint8_t* xbs, float* xrot, void* stream);
+
+/* Offline MXFP4 weight path: wq uint8 [N][K'/2] (16-byte aligned), wbs uint8 [N][K'/32]. */
+CONVROT_API int convrot_quant_weight_mxfp4(const void* w, int32_t w_dtype, int64_t N, int64_t K,
+                                           int64_t g, uint8_t* wq, uint8_t* wbs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

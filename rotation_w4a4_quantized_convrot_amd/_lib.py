@@ -49,6 +49,9 @@ SIGNATURES = {
     "convrot_w8a8_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "convrot_w8a8_linear": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
                                      ctypes.c_size_t, _vp]),
+    "convrot_rotate_quant_act_mxfp4": (_c_int, [_vp, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
+                                                _vp]),
+    "convrot_quant_weight_mxfp4": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -319,3 +322,44 @@ def convrot_w8a8_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Ten
         _ptr(workspace), workspace.numel(), _stream(dev))
     _check(st, g)
     return y
+
+
+def convrot_rotate_quant_act_mxfp4(x: torch.Tensor, g: int, xq: Optional[torch.Tensor] = None,
+                                   xbs: Optional[torch.Tensor] = None,
+                                   xrot: Optional[torch.Tensor] = None, want_rotated: bool = False):
+    """x [M, K] (bf16/fp32, row stride x.stride(0)) -> (xq uint8 [M, K'/2] E2M1 codes,
+    xbs uint8 [M, K'/32] E8M0 block scales[, xrot fp32 [M, K']])."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    Kp = convrot_padded_k(K, g)
+    dev = _require_device(x, xq, xbs, xrot)
+    if xq is None:
+        xq = torch.empty((M, Kp // 2), dtype=torch.uint8, device=dev)
+    if xbs is None:
+        xbs = torch.empty((M, Kp // 32), dtype=torch.uint8, device=dev)
+    if xrot is None and want_rotated:
+        xrot = torch.empty((M, Kp), dtype=torch.float32, device=dev)
+    st = load_library().convrot_rotate_quant_act_mxfp4(
+        _ptr(x), _dtype_code(x), M, K, x.stride(0), g, _ptr(xq), _ptr(xbs), _ptr(xrot),
+        _stream(dev))
+    _check(st, g)
+    return (xq, xbs, xrot) if xrot is not None else (xq, xbs)
+
+
+def convrot_quant_weight_mxfp4(w: torch.Tensor, g: int, wq: Optional[torch.Tensor] = None,
+                               wbs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """w [N, K] contiguous (bf16/fp32) -> (wq uint8 [N, K'/2], wbs uint8 [N, K'/32])."""
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D tensor")
+    N, K = w.shape
+    Kp = convrot_padded_k(K, g)
+    dev = _require_device(w, wq, wbs)
+    if wq is None:
+        wq = torch.empty((N, Kp // 2), dtype=torch.uint8, device=dev)
+    if wbs is None:
+        wbs = torch.empty((N, Kp // 32), dtype=torch.uint8, device=dev)
+    st = load_library().convrot_quant_weight_mxfp4(_ptr(w), _dtype_code(w), N, K, g, _ptr(wq),
+                                                   _ptr(wbs), _stream(dev))
+    _check(st, g)
+    return wq, wbs

@@ -54,9 +54,10 @@ int check_group(int64_t g) {
 int status_of(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_HIP; }
 
 // Validates a rotate+quantize call; on success *kp_out = K'.
+// s: the per-row scales (4-byte aligned), or the MXFP4 block-scale bytes (s_align 1).
 int validate_rq(const void* x, int32_t dtype, int64_t M, int64_t K, int64_t ldx, int64_t g,
-                const uint8_t* q, const float* s, const float* xrot, int64_t* kp_out,
-                int qbits = 4) {
+                const uint8_t* q, const void* s, const float* xrot, int64_t* kp_out,
+                int qbits = 4, size_t s_align = 4) {
   int st = check_group(g);
   if (st != CONVROT_OK) return st;
   if (elem_size(dtype) == 0) return CONVROT_ERR_DTYPE;
@@ -70,7 +71,7 @@ int validate_rq(const void* x, int32_t dtype, int64_t M, int64_t K, int64_t ldx,
     return CONVROT_OK;
   }
   if (x == nullptr || q == nullptr || s == nullptr) return CONVROT_ERR_NULL;
-  if (!aligned(x, (size_t)elem_size(dtype)) || !aligned(q, 16) || !aligned(s, 4) ||
+  if (!aligned(x, (size_t)elem_size(dtype)) || !aligned(q, 16) || !aligned(s, s_align) ||
       (xrot != nullptr && !aligned(xrot, 16)))
     return CONVROT_ERR_ALIGN;
   *kp_out = kp;
@@ -149,8 +150,9 @@ int convrot_rotate_quant_act(const void* x, int32_t x_dtype, int64_t M, int64_t 
   const int st = validate_rq(x, x_dtype, M, K, ldx, g, xq, xs, xrot, &kp);
   if (st != CONVROT_OK || M == 0) return st;
   const int vec = vector_width(x, ldx * elem_size(x_dtype));
-  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp, 4, vec, xq,
-                                                xs, xrot, static_cast<hipStream_t>(stream)));
+  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp,
+                                                convrot::kFmtInt4, vec, xq, xs, nullptr, xrot,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int convrot_rotate_quant_act_i8(const void* x, int32_t x_dtype, int64_t M, int64_t K,
@@ -161,8 +163,27 @@ int convrot_rotate_quant_act_i8(const void* x, int32_t x_dtype, int64_t M, int64
   const int st = validate_rq(x, x_dtype, M, K, ldx, g, q, xs, xrot, &kp, 8);
   if (st != CONVROT_OK || M == 0) return st;
   const int vec = vector_width(x, ldx * elem_size(x_dtype));
-  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp, 8, vec, q, xs,
-                                                xrot, static_cast<hipStream_t>(stream)));
+  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp,
+                                                convrot::kFmtInt8, vec, q, xs, nullptr, xrot,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int convrot_rotate_quant_act_mxfp4(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                   int64_t ldx, int64_t g, uint8_t* xq, uint8_t* xbs,
+                                   float* xrot, void* stream) {
+  if (g == 16) return CONVROT_ERR_UNSUPPORTED;  // a 32-value block would span two windows
+  int64_t kp = 0;
+  const int st = validate_rq(x, x_dtype, M, K, ldx, g, xq, xbs, xrot, &kp, 4, 1);
+  if (st != CONVROT_OK || M == 0) return st;
+  const int vec = vector_width(x, ldx * elem_size(x_dtype));
+  return status_of(convrot::launch_rotate_quant(x, x_dtype, M, K, ldx, (int)g, kp,
+                                                convrot::kFmtMx4, vec, xq, nullptr, xbs, xrot,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int convrot_quant_weight_mxfp4(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t g,
+                               uint8_t* wq, uint8_t* wbs, void* stream) {
+  return convrot_rotate_quant_act_mxfp4(w, w_dtype, N, K, K, g, wq, wbs, nullptr, stream);
 }
 
 int convrot_quant_weight_i8(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t g,
@@ -214,8 +235,8 @@ int convrot_w8a8_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
   if (st != CONVROT_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int vec = vector_width(x, K * elem_size(x_dtype));
-  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, 8, vec, xq, xs,
-                                              nullptr, s);
+  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, convrot::kFmtInt8,
+                                              vec, xq, xs, nullptr, nullptr, s);
   if (e != hipSuccess) return CONVROT_ERR_HIP;
   e = convrot::launch_w8a8_gemm(xq, xs, wb, ws, static_cast<const uint16_t*>(bias), M, N, kp,
                                 static_cast<uint16_t*>(y), nullptr, s);
@@ -269,8 +290,8 @@ int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
   if (st != CONVROT_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int vec = vector_width(x, K * elem_size(x_dtype));
-  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, 4, vec, xq, xs,
-                                              nullptr, s);
+  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, convrot::kFmtInt4,
+                                              vec, xq, xs, nullptr, nullptr, s);
   if (e != hipSuccess) return CONVROT_ERR_HIP;
   const int gvec = ((kp / 2) % 16 == 0) ? 16 : 8;
   e = convrot::launch_w4a4_gemm(xq, xs, wq, ws, static_cast<const uint16_t*>(bias), M, N, kp,

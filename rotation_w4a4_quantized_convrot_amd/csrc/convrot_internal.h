@@ -6,14 +6,19 @@
 
 namespace convrot {
 
-// Launches the fused pad + group-wise RHT + per-row absmax + quantize + pack kernel on rows
-// [0, M) of x (row stride ldx elements).  g in {16, 64, 256, 1024}; Kp = K' <= 65536.
-// x_dtype: 0 = fp32, 1 = bf16.  qbits: 4 (int4 codes, K'/2 bytes per row, scale = max/7) or
-// 8 (int8 codes, K' bytes per row, scale = max/127).  vec_bytes: bytes per input load, 16
-// (every element dword aligned) or 2 (bf16 rows at odd element offsets).
+// Code formats of the rotate+quantize kernel.
+constexpr int kFmtInt4 = 4;  // int4 codes, K'/2 bytes per row, row scale s = max/7
+constexpr int kFmtInt8 = 8;  // int8 codes, K' bytes per row, row scale s = max/127
+constexpr int kFmtMx4 = 1;   // MXFP4: E2M1 codes, K'/2 bytes per row, E8M0 bytes bs[M][K'/32]
+
+// Launches the fused pad + group-wise RHT + absmax + quantize + pack kernel on rows [0, M)
+// of x (row stride ldx elements).  g in {16, 64, 256, 1024} (MXFP4: 64, 256, 1024);
+// Kp = K' <= 65536.  x_dtype: 0 = fp32, 1 = bf16.  fmt: a kFmt* value; s is used by the
+// integer formats, bs by MXFP4.  vec_bytes: bytes per input load, 16 (every element dword
+// aligned) or 2 (bf16 rows at odd element offsets).
 hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                               int g, int64_t Kp, int qbits, int vec_bytes, uint8_t* q, float* s,
-                               float* xrot, hipStream_t stream);
+                               int g, int64_t Kp, int fmt, int vec_bytes, uint8_t* q, float* s,
+                               uint8_t* bs, float* xrot, hipStream_t stream);
 
 // Launches the W4A4 GEMM with the fused dequant epilogue.  vec_bytes: 16 when the packed
 // row stride Kp/2 is a multiple of 16 bytes, else 8.

@@ -360,12 +360,17 @@ __device__ __forceinline__ float candidate_slack() {
 // the row scale (which needs the exact maximum) is stored one iteration later.
 // MW: most waves per workgroup (launch bound 64 MW).  g = 1024 holds 64 values per lane and
 // needs the registers of 8-wave workgroups; rows too long for 8 waves take MW = 16.
-template <int G, typename TIn, int VEC, int QB, int MW>
+// FMT: kFmtInt4, kFmtInt8 (per-row scale s) or kFmtMx4 (MXFP4: E2M1 codes, one E8M0 byte per
+// 32 values in bs, no row scale and no cross-wave reduction).
+template <int G, typename TIn, int VEC, int FMT, int MW>
 __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restrict__ x, int M, int K,
                                                          long ldx, int Kp, int W, int R,
                                                          int nblocks, uint8_t* __restrict__ q,
                                                          float* __restrict__ s,
+                                                         uint8_t* __restrict__ bs,
                                                          float* __restrict__ xrot) {
+  constexpr bool kMx = FMT == kFmtMx4;
+  constexpr int QB = FMT == kFmtInt8 ? 8 : 4;  // bits per code
   constexpr int L = Geo<G>::L, E = Geo<G>::E, C = E / 8, U = 64 / L;
   constexpr int ES = sizeof(TIn);
   // QB = code width: 4 (int4, two codes per byte) or 8 (int8, one code per byte).
@@ -429,7 +434,7 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
 #pragma unroll
       for (int r = 0; r < C; ++r) mask_tail<TIn>(raw[r], j * G + 8 * chunk_of<G>(lu, r), Kc);
     }
-    {  // raw window data, in position order, for the exact recomputation below
+    if constexpr (!kMx) {  // raw window data, in position order, for the exact recomputation
       uint8_t* wb = rawwin + (wave * U + unit) * (G * ES);
 #pragma unroll
       for (int r = 0; r < C; ++r) {
@@ -464,9 +469,42 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
       cm[r] = c;
       ml = fmaxf(ml, c);
     }
+    uint32_t packed[C][QB / 4];  // the chunk's 8 codes: one dword (4-bit) or two (int8)
+    float mrow = 0.0f;
+    uint32_t* rexact = red;
+    if constexpr (kMx) {
+      // MXFP4 (OCP Microscaling v1.0): a 32-value block is chunks r, r ^ 1 of this lane and
+      // of the lane with position bit 3 flipped (xor 1); its E8M0 byte is
+      // floor(log2(absmax)) - 2 + 127, i.e. absmax's exponent field - 2, clamped at 0.  The
+      // conversion divides by the block scale, rounds to nearest even and saturates at 6.
+#pragma unroll
+      for (int r = 0; r < C; r += 2) {
+        float bm = fmaxf(cm[r], cm[r + 1]);
+        bm = fmaxf(bm, dpp_f32<kDppXor1>(bm));
+        const int eb = max(int(__float_as_uint(bm) >> 23) - 2, 0);
+        const float xs = eb > 0 ? __uint_as_float(uint32_t(eb) << 23) : 0x1p-127f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t o = 0;
+          const float* vv = &v[8 * (r + h)];
+          o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, vv[0], vv[1], xs, 0);
+          o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, vv[2], vv[3], xs, 1);
+          o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, vv[4], vv[5], xs, 2);
+          o = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(o, vv[6], vv[7], xs, 3);
+          packed[r + h][0] = o;
+        }
+        const int ch = chunk_of<G>(lu, r);
+        if (active && (ch & 1) == 0) {  // one of the two lanes stores the block's byte
+          const __amdgpu_buffer_rsrc_t bsr = make_rsrc(bs, long(M) * (Kp / 32));
+          __builtin_amdgcn_raw_buffer_store_b8(uint8_t(eb), bsr,
+                                               uint32_t(m * (Kp / 32) + j * (G / 32) + (ch >> 2)),
+                                               0, 0);
+        }
+      }
+    } else {
     const float mu = unit_max<L>(ml);
     uint32_t* rmax = red + (it & 3) * 2 * R;
-    uint32_t* rexact = rmax + R;
+    rexact = rmax + R;
     if (active && lu == 0) atomicMax(&rmax[rloc], __float_as_uint(mu));
     __syncthreads();
 
@@ -479,9 +517,8 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
     }
 
     // Codes use the fp32 maximum; they agree with the exact one except at rounding ties.
-    const float mrow = slot_used ? __uint_as_float(rmax[rloc < R ? rloc : 0]) : 0.0f;
+    mrow = slot_used ? __uint_as_float(rmax[rloc < R ? rloc : 0]) : 0.0f;
     const float inv = mrow > 0.0f ? kQmax / mrow : 0.0f;
-    uint32_t packed[C][QB / 4];  // the chunk's 8 codes: one dword (int4) or two (int8)
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       uint32_t bits[8];
@@ -500,6 +537,7 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
         packed[r][0] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
         packed[r][1] = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
       }
+    }
     }
     // Transpose the unit's packed window through this wave's LDS slice so every lane
     // stores contiguous bytes (wave-local: LDS operations of one wave complete in order).
@@ -542,7 +580,7 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
     // Exact maxima: every element within the butterfly's error bound of the row's fp32
     // maximum is recomputed exactly (see candidate_slack); usually one per row.
     const float thr = mrow - (mrow * candidate_slack<G>() + 1e-37f);
-    const bool live = active && mrow > 0.0f;
+    const bool live = !kMx && active && mrow > 0.0f;
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       uint64_t cand = __ballot(live && cm[r] >= thr);
@@ -571,9 +609,11 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
     }
     prev_m = active ? m : -1;
   }
-  __syncthreads();
-  if (prev_m >= 0 && lu == 0 && j == 0)
-    s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / kQmax;
+  if constexpr (!kMx) {
+    __syncthreads();
+    if (prev_m >= 0 && lu == 0 && j == 0)
+      s[prev_m] = __uint_as_float(red[((it - 1) & 3) * 2 * R + R + rloc]) / kQmax;
+  }
 }
 
 struct RqPlan {
@@ -584,17 +624,19 @@ struct RqPlan {
 // the workgroup's LDS (per-row reduction slots + per-wave staging) within the 160 KiB of a CU.
 constexpr size_t kMaxLds = 160 * 1024;
 
-size_t rq_shmem(int R, int waves, int U, int G, int esize, int qb) {
+// qb: bits per code; raw: whether the raw input windows are staged for the exact maxima
+// (the integer formats).
+size_t rq_shmem(int R, int waves, int U, int G, int esize, int qb, bool raw) {
   return size_t((8 * R + 3) & ~3) * 4 + size_t(waves) * U * (G * qb / 8) +
-         size_t(waves) * U * G * esize;
+         (raw ? size_t(waves) * U * G * esize : 0);
 }
 
-RqPlan plan_rows(int W, int U, int G, int esize, int qb, int max_waves) {
+RqPlan plan_rows(int W, int U, int G, int esize, int qb, bool raw, int max_waves) {
   RqPlan best{1, (W + U - 1) / U};
   double best_eff = double(W) / (best.waves * U);
   for (int R = 2; R <= 64; ++R) {
     const int waves = (R * W + U - 1) / U;
-    if (waves > max_waves || rq_shmem(R, waves, U, G, esize, qb) > kMaxLds) break;
+    if (waves > max_waves || rq_shmem(R, waves, U, G, esize, qb, raw) > kMaxLds) break;
     const double eff = double(R * W) / (waves * U);
     if (eff > best_eff + 1e-9) {
       best = {R, waves};
@@ -616,9 +658,12 @@ int device_cus() {
   return n;
 }
 
-template <int G, typename TIn, int VEC, int QB, int MW>
+template <int FMT>
+constexpr int fmt_bits() { return FMT == kFmtInt8 ? 8 : 4; }
+
+template <int G, typename TIn, int VEC, int FMT, int MW>
 hipError_t launch_plan(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp, RqPlan p,
-                       uint8_t* q, float* s, float* xrot, hipStream_t stream) {
+                       uint8_t* q, float* s, uint8_t* bs, float* xrot, hipStream_t stream) {
   constexpr int L = Geo<G>::L, U = 64 / L;
   const int W = int(Kp / G);
   // Byte offsets inside a block are 32-bit: keep R rows of stride ldx below 2 GiB.
@@ -627,10 +672,13 @@ hipError_t launch_plan(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t 
     p.waves = (W + U - 1) / U;
   }
   if (p.waves > MW || ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  // MXFP4 block-scale bytes are addressed with 32-bit offsets from bs.
+  if (FMT == kFmtMx4 && M * (Kp / 32) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int nblocks = int((M + p.R - 1) / p.R);
-  const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)), QB);
+  const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)), fmt_bits<FMT>(),
+                                FMT != kFmtMx4);
   if (shmem > kMaxLds) return hipErrorInvalidValue;
-  auto kernel = rht_quant_kernel<G, TIn, VEC, QB, MW>;
+  auto kernel = rht_quant_kernel<G, TIn, VEC, FMT, MW>;
   if (shmem > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, int(shmem));
@@ -642,48 +690,53 @@ hipError_t launch_plan(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t 
     per_cu = 1;
   const int grid = int(std::min<int64_t>(nblocks, int64_t(device_cus()) * per_cu));
   return launch_kernel(kernel, dim3(unsigned(grid)), dim3(unsigned(64 * p.waves)), shmem, stream,
-                       x, int(M), int(K), long(ldx), int(Kp), W, p.R, nblocks, q, s, xrot);
+                       x, int(M), int(K), long(ldx), int(Kp), W, p.R, nblocks, q, s, bs, xrot);
 }
 
-template <int G, typename TIn, int VEC, int QB>
+template <int G, typename TIn, int VEC, int FMT>
 hipError_t launch_g(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t Kp, uint8_t* q,
-                    float* s, float* xrot, hipStream_t stream) {
+                    float* s, uint8_t* bs, float* xrot, hipStream_t stream) {
   constexpr int L = Geo<G>::L, U = 64 / L;
   const int W = int(Kp / G);
   const int es = int(sizeof(TIn));
+  constexpr int qb = fmt_bits<FMT>();
+  constexpr bool raw = FMT != kFmtMx4;
   if constexpr (G == 1024) {
-    const RqPlan p8 = plan_rows(W, U, G, es, QB, 8);
+    const RqPlan p8 = plan_rows(W, U, G, es, qb, raw, 8);
     if (p8.waves <= 8)
-      return launch_plan<G, TIn, VEC, QB, 8>(x, M, K, ldx, Kp, p8, q, s, xrot, stream);
+      return launch_plan<G, TIn, VEC, FMT, 8>(x, M, K, ldx, Kp, p8, q, s, bs, xrot, stream);
   }
-  return launch_plan<G, TIn, VEC, QB, 16>(x, M, K, ldx, Kp, plan_rows(W, U, G, es, QB, 16), q, s,
-                                          xrot, stream);
+  return launch_plan<G, TIn, VEC, FMT, 16>(x, M, K, ldx, Kp, plan_rows(W, U, G, es, qb, raw, 16),
+                                           q, s, bs, xrot, stream);
 }
 
-template <typename TIn, int VEC, int QB>
+template <typename TIn, int VEC, int FMT>
 hipError_t launch_gq(const TIn* x, int64_t M, int64_t K, int64_t ldx, int g, int64_t Kp,
-                     uint8_t* q, float* s, float* xrot, hipStream_t st) {
+                     uint8_t* q, float* s, uint8_t* bs, float* xrot, hipStream_t st) {
   switch (g) {
-    case 16: return launch_g<16, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
-    case 64: return launch_g<64, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
-    case 256: return launch_g<256, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
-    case 1024: return launch_g<1024, TIn, VEC, QB>(x, M, K, ldx, Kp, q, s, xrot, st);
+    case 16:
+      if constexpr (FMT == kFmtMx4) return hipErrorInvalidValue;  // blocks span two windows
+      else return launch_g<16, TIn, VEC, FMT>(x, M, K, ldx, Kp, q, s, bs, xrot, st);
+    case 64: return launch_g<64, TIn, VEC, FMT>(x, M, K, ldx, Kp, q, s, bs, xrot, st);
+    case 256: return launch_g<256, TIn, VEC, FMT>(x, M, K, ldx, Kp, q, s, bs, xrot, st);
+    case 1024: return launch_g<1024, TIn, VEC, FMT>(x, M, K, ldx, Kp, q, s, bs, xrot, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename TIn, int VEC>
-hipError_t launch_t(const TIn* x, int64_t M, int64_t K, int64_t ldx, int g, int64_t Kp,
-                    int qbits, uint8_t* q, float* s, float* xrot, hipStream_t st) {
-  if (qbits == 8) return launch_gq<TIn, VEC, 8>(x, M, K, ldx, g, Kp, q, s, xrot, st);
-  return launch_gq<TIn, VEC, 4>(x, M, K, ldx, g, Kp, q, s, xrot, st);
+hipError_t launch_t(const TIn* x, int64_t M, int64_t K, int64_t ldx, int g, int64_t Kp, int fmt,
+                    uint8_t* q, float* s, uint8_t* bs, float* xrot, hipStream_t st) {
+  if (fmt == kFmtInt8) return launch_gq<TIn, VEC, kFmtInt8>(x, M, K, ldx, g, Kp, q, s, bs, xrot, st);
+  if (fmt == kFmtMx4) return launch_gq<TIn, VEC, kFmtMx4>(x, M, K, ldx, g, Kp, q, s, bs, xrot, st);
+  return launch_gq<TIn, VEC, kFmtInt4>(x, M, K, ldx, g, Kp, q, s, bs, xrot, st);
 }
 
 }  // namespace
 
 hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
-                               int g, int64_t Kp, int qbits, int vec_bytes, uint8_t* q, float* s,
-                               float* xrot, hipStream_t stream) {
+                               int g, int64_t Kp, int fmt, int vec_bytes, uint8_t* q, float* s,
+                               uint8_t* bs, float* xrot, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (x_dtype == 1) {
     // Buffer range checks are per dword: if the last valid bf16 element shares a dword with
@@ -691,11 +744,11 @@ hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K,
     if ((((M - 1) * ldx + K) & 1) != 0) vec_bytes = 2;
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     if (vec_bytes == 16)
-      return launch_t<uint16_t, 16>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
-    return launch_t<uint16_t, 2>(xb, M, K, ldx, g, Kp, qbits, q, s, xrot, stream);
+      return launch_t<uint16_t, 16>(xb, M, K, ldx, g, Kp, fmt, q, s, bs, xrot, stream);
+    return launch_t<uint16_t, 2>(xb, M, K, ldx, g, Kp, fmt, q, s, bs, xrot, stream);
   }
   // fp32 elements are dword aligned: always 16-byte loads
-  return launch_t<float, 16>(static_cast<const float*>(x), M, K, ldx, g, Kp, qbits, q, s, xrot,
+  return launch_t<float, 16>(static_cast<const float*>(x), M, K, ldx, g, Kp, fmt, q, s, bs, xrot,
                              stream);
 }
 

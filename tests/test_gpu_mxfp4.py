@@ -1,0 +1,147 @@
+"""MXFP4 ConvRot on the GPU vs the CPU oracle, through the C ABI (needs a gfx950 GPU).
+
+Bars (derived from the arithmetic; the kernel's block maxima come from its fp32 rotation,
+whose error is a few ulp of the row maximum, not from the exact rotation):
+  * rotated activations within 1e-5 of the oracle (row relative);
+  * a block's E8M0 byte may differ from the oracle's only by one, only where the oracle's
+    block maximum lies within 2^-12 (in log2) of a power of two, in at most 1e-3 of blocks;
+  * within blocks of equal scale a code may differ only where value / scale lies within the
+    rotation's error of an E2M1 rounding tie, by one step, in at most 1e-3 of the codes
+    (codes are compared by value: +0 and -0 are the same number).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wk
+from oracle import convrot_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ROT_REL_MAX = 1e-5
+BLOCK_MISMATCH_MAX = 1e-3
+CODE_MISMATCH_MAX = 1e-3
+TIES = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotation_w4a4_quantized_convrot_amd as mod
+    mod.load_library()  # raises if the HIP library is missing: no fallback
+    return mod
+
+
+def _to_dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).to(DEV)
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check_mx(gpu_q, gpu_bs, gpu_rot, ref, label="", max_frac=CODE_MISMATCH_MAX):
+    yf = ref["yf"].astype(np.float64)
+    rows, kp = yf.shape
+    bs = gpu_bs.cpu().numpy()
+    assert bs.dtype == np.uint8 and bs.shape == ref["scales"].shape
+    db = bs.astype(np.int64) - ref["scales"].astype(np.int64)
+    bad = np.nonzero(db)
+    if len(bad[0]):
+        assert np.max(np.abs(db)) <= 1, f"{label}: block scale off by {np.max(np.abs(db))}"
+        amax = np.abs(yf.reshape(rows, kp // 32, 32)).max(axis=2)[bad]
+        l2 = np.log2(amax)
+        assert np.all(np.abs(l2 - np.round(l2)) <= 2.0 ** -12), \
+            f"{label}: a block scale differs away from a power of two"
+    assert len(bad[0]) <= BLOCK_MISMATCH_MAX * bs.size + 0, f"{label}: {len(bad[0])} blocks differ"
+    q = O.unpack_int4(gpu_q.cpu().numpy()).astype(np.int64) & 0xF
+    same = np.repeat(db == 0, 32, axis=1)
+    vg = O.e2m1_decode(q)
+    vo = O.e2m1_decode(ref["codes"])
+    diff = (vg != vo) & same
+    r_i, c_i = np.nonzero(diff)
+    if len(r_i):
+        grid = O.E2M1_GRID
+        step = np.abs(np.searchsorted(grid, np.abs(vg[r_i, c_i])) -
+                      np.searchsorted(grid, np.abs(vo[r_i, c_i])))
+        assert np.all(step <= 1) and np.all(np.sign(vg[r_i, c_i]) * np.sign(vo[r_i, c_i]) >= 0), \
+            f"{label}: a code differs by more than one step"
+        x_scale = np.exp2(ref["scales"].astype(np.float64) - 127)[r_i, c_i // 32]
+        t = np.abs(yf[r_i, c_i]) / x_scale
+        rowmax = np.abs(yf).max(axis=1)[r_i]
+        near = np.min(np.abs(t[:, None] - TIES[None, :]), axis=1)
+        assert np.all(near <= 2.0 ** -14 * rowmax / x_scale + 1e-12), \
+            f"{label}: a code differs away from a rounding tie"
+    frac = len(r_i) / max(q.size, 1)
+    assert frac <= max_frac, f"{label}: {frac:.2e} codes differ"
+    if gpu_rot is not None:
+        r = gpu_rot.cpu().numpy()
+        den = np.max(np.abs(yf), axis=1)
+        num = np.max(np.abs(r - yf), axis=1)
+        rel = np.where(den > 0, num / np.where(den > 0, den, 1), num)
+        assert np.max(rel) <= ROT_REL_MAX, f"{label}: rotated rel err {np.max(rel):.2e}"
+
+
+ROTATE_CASES = [
+    # M, K, g, dtype
+    (7, 200, 64, "f32"), (130, 1000, 64, "bf16"), (200, 3072, 256, "bf16"),
+    (37, 3100, 256, "bf16"), (33, 777, 256, "f32"), (48, 12288, 1024, "bf16"),
+    (23, 3000, 1024, "bf16"), (3, 61440, 1024, "bf16"), (2, 32768, 1024, "f32"),
+    (2, 32768, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,K,g,dtype", ROTATE_CASES)
+def test_rotate_quant_mxfp4_parity(cr, M, K, g, dtype):
+    _announce(f"rotate_quant_mxfp4 M={M} K={K} g={g} {dtype}")
+    wl = wk.custom("t", M, K, None, g, x_dtype=dtype)
+    x = wk.activations(wl)
+    ref = O.rotate_quantize_mxfp4(x, g)
+    xq, xbs, xr = cr.convrot_rotate_quant_act_mxfp4(_to_dev(x, dtype), g, want_rotated=True)
+    torch.cuda.synchronize()
+    check_mx(xq, xbs, xr, ref, f"M={M} K={K} g={g}")
+
+
+@pytest.mark.parametrize("g", [64, 256, 1024])
+def test_rotate_quant_mxfp4_edge_rows(cr, g):
+    """Zero rows and blocks, constant rows, a single spike, tiny values, huge values."""
+    _announce(f"mxfp4 edge rows g={g}")
+    K = 2 * g + g // 2
+    x = np.zeros((7, K), dtype=np.float32)
+    x[1, :] = 1.5
+    x[2, :] = -0.375
+    x[3, 5] = 1000.0
+    x[4, :] = np.arange(K) % 9 - 4.0
+    x[5, : g // 2] = 2.0 ** -20
+    x[6, :] = 3.0e38 / g
+    ref = O.rotate_quantize_mxfp4(x, g)
+    xq, xbs = cr.convrot_rotate_quant_act_mxfp4(_to_dev(x, "f32"), g)
+    torch.cuda.synchronize()
+    check_mx(xq, xbs, None, ref, "edge", max_frac=1.0)
+    assert torch.all(xq[0] == 0) and torch.all(xbs[0] == 0)
+
+
+def test_mxfp4_weights_and_strides(cr):
+    _announce("mxfp4 weights, strided rows")
+    wl = wk.custom("t", 50, 1100, 96, 256)
+    w = wk.weights(wl)
+    ref = O.quantize_weight_mxfp4(w, 256)
+    wq, wbs = cr.convrot_quant_weight_mxfp4(_to_dev(w, "bf16"), 256)
+    torch.cuda.synchronize()
+    check_mx(wq, wbs, None, ref, "weights")
+    x = wk.activations(wl)
+    big = torch.zeros((50, 1200), dtype=torch.bfloat16, device=DEV)
+    big[:, :1100] = _to_dev(x, "bf16")
+    xq, xbs = cr.convrot_rotate_quant_act_mxfp4(big[:, :1100], 256)
+    torch.cuda.synchronize()
+    check_mx(xq, xbs, None, O.rotate_quantize_mxfp4(x, 256), "strided")
+
+
+def test_mxfp4_rejects_group_16(cr):
+    with pytest.raises(cr.ConvRotError):
+        cr.convrot_rotate_quant_act_mxfp4(torch.zeros((2, 64), dtype=torch.bfloat16, device=DEV), 16)
