@@ -205,7 +205,8 @@ CONVROT_API int convrot_w8a8_linear(const void* x, int32_t x_dtype, int64_t M, i
  * all-zero block takes 0), and each value becomes the E2M1 code nearest to value / 2^(e-127),
  * ties to the even mantissa, magnitudes beyond 6 saturating at 6, the sign bit following the
  * value (-0.0 -> 0x8).  Codes: two per byte, value 2j in the low nibble, row stride K'/2
- * bytes; scales: row stride K'/32 bytes.  The block maxima are those of the fp32 rotation:
+ * bytes; scales: K'/32 bytes per row in rows of S = 4 ceil(K'/128) bytes (S = K'/32 unless
+ * g = 64; the padding bytes are written as 0).  The block maxima are those of the fp32 rotation:
  * a block's exponent may differ from the definition's only where its maximum lies within
  * the rotation's rounding error of a power of two, and a code only at a rounding tie.
  * g must be 64, 256 or 1024 (g = 16: UNSUPPORTED).
@@ -213,16 +214,42 @@ CONVROT_API int convrot_w8a8_linear(const void* x, int32_t x_dtype, int64_t M, i
 
 /* Online activation path, MXFP4: as convrot_rotate_quant_act, with
  *   xq   device, uint8 [M][K'/2] E2M1 codes, 16-byte aligned;
- *   xbs  device, uint8 [M][K'/32] E8M0 block scales (no alignment).
+ *   xbs  device, uint8 [M][S] E8M0 block scales, S = 4 ceil(K'/128) (no alignment).
  * K' limits as for int4 codes.  M = 0 is a no-op.
  * Errors: GROUP, UNSUPPORTED, SHAPE, NULL, DTYPE, ALIGN, HIP. */
 CONVROT_API int convrot_rotate_quant_act_mxfp4(const void* x, int32_t x_dtype, int64_t M,
                                                int64_t K, int64_t ldx, int64_t g, uint8_t* xq,
                                                uint8_t* xbs, float* xrot, void* stream);
 
-/* Offline MXFP4 weight path: wq uint8 [N][K'/2] (16-byte aligned), wbs uint8 [N][K'/32]. */
+/* Offline MXFP4 weight path: wq uint8 [N][K'/2] (16-byte aligned), wbs uint8 [N][S]. */
 CONVROT_API int convrot_quant_weight_mxfp4(const void* w, int32_t w_dtype, int64_t N, int64_t K,
                                            int64_t g, uint8_t* wq, uint8_t* wbs, void* stream);
+
+/* MXFP4 GEMM (gfx950's scaled FP4 matrix instructions, fp32 accumulation):
+ *   y[m][n] = bf16( fp32( sum_k x[m][k] w[n][k] ) + bias[n] ), x and w the decoded values
+ *   (E2M1 code * 2^(E8M0 - 127) of its block).
+ *   xq [M][Kp/2], wq [N][Kp/2] packed codes (16-byte aligned); xbs [M][S], wbs [N][S] E8M0
+ *   bytes, S = 4 ceil(Kp/128) (4-byte aligned); bias bf16 [N] or NULL; y bf16 [M][N] (4-byte
+ *   aligned); Kp a positive multiple of 64, <= CONVROT_MAX_KP; acc_dbg fp32 [M][N] (16-byte
+ *   aligned) receives the sums before the bias, or NULL.
+ * The order in which the hardware adds the products is not specified: the sum carries fp32
+ * rounding of at most about Kp/64 roundings of partial sums, not an exact result.
+ * M = 0 or N = 0 is a no-op.  Errors: SHAPE, NULL, ALIGN, UNSUPPORTED, HIP. */
+CONVROT_API int convrot_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_t* wq,
+                                   const uint8_t* wbs, const void* bias, int64_t M, int64_t N,
+                                   int64_t Kp, void* y, float* acc_dbg, void* stream);
+
+/* Bytes of device workspace convrot_mxfp4_linear needs: codes M*K'/2 and scales M*S, each
+ * rounded up to 256 bytes.  Returns 0 for an invalid or unsupported g or shape. */
+CONVROT_API size_t convrot_mxfp4_workspace_bytes(int64_t M, int64_t K, int64_t g);
+
+/* The MXFP4 forward pass: rotate + quantize x to MXFP4 in the workspace, then the MXFP4 GEMM
+ * against wq / wbs (from convrot_quant_weight_mxfp4 with the same g and K), writing y bf16
+ * [M][N].  Arguments and errors as for convrot_w4a4_linear; g = 16 is UNSUPPORTED. */
+CONVROT_API int convrot_mxfp4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                     int64_t g, const uint8_t* wq, const uint8_t* wbs, int64_t N,
+                                     const void* bias, void* y, void* workspace, size_t ws_bytes,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

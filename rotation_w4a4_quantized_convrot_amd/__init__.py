@@ -10,7 +10,8 @@ from ._lib import (  # noqa: F401
     convrot_w4a4_linear, convrot_w4a4_workspace_bytes, load_library,
     convrot_quant_weight_i8, convrot_rotate_quant_act_i8, convrot_w8a8_gemm,
     convrot_w8a8_linear, convrot_w8a8_workspace_bytes,
-    convrot_rotate_quant_act_mxfp4, convrot_quant_weight_mxfp4,
+    convrot_rotate_quant_act_mxfp4, convrot_quant_weight_mxfp4, convrot_mxfp4_gemm,
+    convrot_mxfp4_workspace_bytes, convrot_mxfp4_linear, mx_scale_stride,
 )
 from .linear import ConvLinear4bit  # noqa: F401
 
@@ -20,5 +21,6 @@ __all__ = [
     "convrot_quant_weight", "convrot_w4a4_gemm", "convrot_w4a4_workspace_bytes",
     "convrot_w4a4_linear", "convrot_rotate_quant_act_i8", "convrot_quant_weight_i8",
     "convrot_w8a8_gemm", "convrot_w8a8_workspace_bytes", "convrot_w8a8_linear",
-    "convrot_rotate_quant_act_mxfp4", "convrot_quant_weight_mxfp4",
+    "convrot_rotate_quant_act_mxfp4", "convrot_quant_weight_mxfp4", "convrot_mxfp4_gemm",
+    "convrot_mxfp4_workspace_bytes", "convrot_mxfp4_linear",
 ]

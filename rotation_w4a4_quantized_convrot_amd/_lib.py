@@ -52,6 +52,10 @@ SIGNATURES = {
     "convrot_rotate_quant_act_mxfp4": (_c_int, [_vp, _i32, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                                 _vp]),
     "convrot_quant_weight_mxfp4": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "convrot_mxfp4_gemm": (_c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "convrot_mxfp4_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "convrot_mxfp4_linear": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -324,11 +328,17 @@ def convrot_w8a8_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Ten
     return y
 
 
+def mx_scale_stride(kp: int) -> int:
+    """Bytes per row of MXFP4 block scales: K'/32 blocks padded to whole dwords."""
+    return 4 * (-(-kp // 128))
+
+
 def convrot_rotate_quant_act_mxfp4(x: torch.Tensor, g: int, xq: Optional[torch.Tensor] = None,
                                    xbs: Optional[torch.Tensor] = None,
                                    xrot: Optional[torch.Tensor] = None, want_rotated: bool = False):
     """x [M, K] (bf16/fp32, row stride x.stride(0)) -> (xq uint8 [M, K'/2] E2M1 codes,
-    xbs uint8 [M, K'/32] E8M0 block scales[, xrot fp32 [M, K']])."""
+    xbs uint8 [M, S] E8M0 block scales (S = 4 ceil(K'/128): K'/32 blocks, zero padding)
+    [, xrot fp32 [M, K']])."""
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     M, K = x.shape
@@ -337,7 +347,7 @@ def convrot_rotate_quant_act_mxfp4(x: torch.Tensor, g: int, xq: Optional[torch.T
     if xq is None:
         xq = torch.empty((M, Kp // 2), dtype=torch.uint8, device=dev)
     if xbs is None:
-        xbs = torch.empty((M, Kp // 32), dtype=torch.uint8, device=dev)
+        xbs = torch.empty((M, mx_scale_stride(Kp)), dtype=torch.uint8, device=dev)
     if xrot is None and want_rotated:
         xrot = torch.empty((M, Kp), dtype=torch.float32, device=dev)
     st = load_library().convrot_rotate_quant_act_mxfp4(
@@ -349,7 +359,7 @@ def convrot_rotate_quant_act_mxfp4(x: torch.Tensor, g: int, xq: Optional[torch.T
 
 def convrot_quant_weight_mxfp4(w: torch.Tensor, g: int, wq: Optional[torch.Tensor] = None,
                                wbs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """w [N, K] contiguous (bf16/fp32) -> (wq uint8 [N, K'/2], wbs uint8 [N, K'/32])."""
+    """w [N, K] contiguous (bf16/fp32) -> (wq uint8 [N, K'/2], wbs uint8 [N, S])."""
     if w.dim() != 2 or not w.is_contiguous():
         raise ValueError("w must be a contiguous 2-D tensor")
     N, K = w.shape
@@ -358,8 +368,56 @@ def convrot_quant_weight_mxfp4(w: torch.Tensor, g: int, wq: Optional[torch.Tenso
     if wq is None:
         wq = torch.empty((N, Kp // 2), dtype=torch.uint8, device=dev)
     if wbs is None:
-        wbs = torch.empty((N, Kp // 32), dtype=torch.uint8, device=dev)
+        wbs = torch.empty((N, mx_scale_stride(Kp)), dtype=torch.uint8, device=dev)
     st = load_library().convrot_quant_weight_mxfp4(_ptr(w), _dtype_code(w), N, K, g, _ptr(wq),
                                                    _ptr(wbs), _stream(dev))
     _check(st, g)
     return wq, wbs
+
+
+def convrot_mxfp4_gemm(xq: torch.Tensor, xbs: torch.Tensor, wq: torch.Tensor, wbs: torch.Tensor,
+                       bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                       want_acc: bool = False):
+    """MXFP4 GEMM: y bf16 [M, N] (and the fp32 sums [M, N] before the bias if want_acc)."""
+    M, half = xq.shape
+    N = wq.shape[0]
+    Kp = 2 * half
+    if wq.shape[1] != half:
+        raise ValueError("xq and wq must have the same depth")
+    if xbs.shape != (M, mx_scale_stride(Kp)) or wbs.shape != (N, mx_scale_stride(Kp)):
+        raise ValueError("block scales must be [rows, 4 ceil(K'/128)]")
+    if bias is not None and bias.dtype != torch.bfloat16:
+        raise TypeError("bias must be bfloat16")
+    dev = _require_device(xq, xbs, wq, wbs, bias, y)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    acc = torch.empty((M, N), dtype=torch.float32, device=dev) if want_acc else None
+    st = load_library().convrot_mxfp4_gemm(_ptr(xq), _ptr(xbs), _ptr(wq), _ptr(wbs), _ptr(bias), M,
+                                           N, Kp, _ptr(y), _ptr(acc), _stream(dev))
+    _check(st)
+    return (y, acc) if want_acc else y
+
+
+def convrot_mxfp4_workspace_bytes(M: int, K: int, g: int) -> int:
+    return int(load_library().convrot_mxfp4_workspace_bytes(M, K, g))
+
+
+def convrot_mxfp4_linear(x: torch.Tensor, g: int, wq: torch.Tensor, wbs: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The MXFP4 ConvRot forward pass: x [M, K] contiguous -> y bf16 [M, N]."""
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D tensor")
+    M, K = x.shape
+    N = wq.shape[0]
+    dev = _require_device(x, wq, wbs, bias, y, workspace)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    need = convrot_mxfp4_workspace_bytes(M, K, g)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    st = load_library().convrot_mxfp4_linear(_ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(wbs),
+                                             N, _ptr(bias), _ptr(y), _ptr(workspace),
+                                             workspace.numel(), _stream(dev))
+    _check(st, g)
+    return y

@@ -186,6 +186,65 @@ int convrot_quant_weight_mxfp4(const void* w, int32_t w_dtype, int64_t N, int64_
   return convrot_rotate_quant_act_mxfp4(w, w_dtype, N, K, K, g, wq, wbs, nullptr, stream);
 }
 
+int convrot_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_t* wq,
+                       const uint8_t* wbs, const void* bias, int64_t M, int64_t N, int64_t Kp,
+                       void* y, float* acc_dbg, void* stream) {
+  if (M < 0 || N < 0 || Kp < 64 || (Kp % 64) != 0 || M > INT32_MAX || N > INT32_MAX)
+    return CONVROT_ERR_SHAPE;
+  if (Kp > CONVROT_MAX_KP) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (xq == nullptr || xbs == nullptr || wq == nullptr || wbs == nullptr || y == nullptr)
+    return CONVROT_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || !aligned(xbs, 4) || !aligned(wbs, 4) ||
+      !aligned(y, 4) || (bias != nullptr && !aligned(bias, 2)) ||
+      (acc_dbg != nullptr && !aligned(acc_dbg, 16)))
+    return CONVROT_ERR_ALIGN;
+  return status_of(convrot::launch_mxfp4_gemm(xq, xbs, wq, wbs, static_cast<const uint16_t*>(bias),
+                                              M, N, Kp, static_cast<uint16_t*>(y), acc_dbg,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+size_t convrot_mxfp4_workspace_bytes(int64_t M, int64_t K, int64_t g) {
+  if (M < 0 || M > INT32_MAX || g == 16) return 0;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return 0;
+  return round256((size_t)M * (size_t)(kp / 2)) + round256((size_t)M * (size_t)((kp + 127) / 128 * 4));
+}
+
+int convrot_mxfp4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t g,
+                         const uint8_t* wq, const uint8_t* wbs, int64_t N, const void* bias,
+                         void* y, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_group(g);
+  if (st != CONVROT_OK) return st;
+  if (g == 16) return CONVROT_ERR_UNSUPPORTED;
+  if (elem_size(x_dtype) == 0) return CONVROT_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 1 || M > INT32_MAX || N > INT32_MAX) return CONVROT_ERR_SHAPE;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return (int)kp;
+  if (kp > max_row_kp(g, x_dtype, 4)) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (x == nullptr || wq == nullptr || wbs == nullptr || y == nullptr || workspace == nullptr)
+    return CONVROT_ERR_NULL;
+  if (!aligned(workspace, 256)) return CONVROT_ERR_ALIGN;
+  if (ws_bytes < convrot_mxfp4_workspace_bytes(M, K, g)) return CONVROT_ERR_WORKSPACE;
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  uint8_t* xbs = xq + round256((size_t)M * (size_t)(kp / 2));
+  int64_t kp_rq = 0;
+  st = validate_rq(x, x_dtype, M, K, K, g, xq, xbs, nullptr, &kp_rq, 4, 1);
+  if (st != CONVROT_OK) return st;
+  if (!aligned(wq, 16) || !aligned(wbs, 4) || !aligned(y, 4) ||
+      (bias != nullptr && !aligned(bias, 2)))
+    return CONVROT_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int vec = vector_width(x, K * elem_size(x_dtype));
+  hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, convrot::kFmtMx4,
+                                              vec, xq, nullptr, xbs, nullptr, s);
+  if (e != hipSuccess) return CONVROT_ERR_HIP;
+  e = convrot::launch_mxfp4_gemm(xq, xbs, wq, wbs, static_cast<const uint16_t*>(bias), M, N, kp,
+                                 static_cast<uint16_t*>(y), nullptr, s);
+  return status_of(e);
+}
+
 int convrot_quant_weight_i8(const void* w, int32_t w_dtype, int64_t N, int64_t K, int64_t g,
                             int8_t* wq, float* ws, void* stream) {
   return convrot_rotate_quant_act_i8(w, w_dtype, N, K, K, g, wq, ws, nullptr, stream);

@@ -9,7 +9,8 @@ namespace convrot {
 // Code formats of the rotate+quantize kernel.
 constexpr int kFmtInt4 = 4;  // int4 codes, K'/2 bytes per row, row scale s = max/7
 constexpr int kFmtInt8 = 8;  // int8 codes, K' bytes per row, row scale s = max/127
-constexpr int kFmtMx4 = 1;   // MXFP4: E2M1 codes, K'/2 bytes per row, E8M0 bytes bs[M][K'/32]
+constexpr int kFmtMx4 = 1;   // MXFP4: E2M1 codes, K'/2 bytes per row, E8M0 bytes bs[M][S]
+                             // with S = 4 ceil(K'/128) (K'/32 blocks, zero padding)
 
 // Launches the fused pad + group-wise RHT + absmax + quantize + pack kernel on rows [0, M)
 // of x (row stride ldx elements).  g in {16, 64, 256, 1024} (MXFP4: 64, 256, 1024);
@@ -32,6 +33,13 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
 hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq,
                             const float* ws, const uint16_t* bias, int64_t M, int64_t N,
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream);
+
+// Launches the MXFP4 GEMM: packed E2M1 codes (K'/2 bytes per row) with E8M0 block scales
+// (rows of 4 ceil(K'/128) bytes), fp32 accumulation on the scaled FP4 matrix instructions,
+// y = bf16(sum + bias).  Kp must be a multiple of 64.  acc_dbg: the fp32 sums, or NULL.
+hipError_t launch_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_t* wq,
+                             const uint8_t* wbs, const uint16_t* bias, int64_t M, int64_t N,
+                             int64_t Kp, uint16_t* y, float* acc_dbg, hipStream_t stream);
 
 // Small launch helper that returns the launch status instead of relying on hipGetLastError.
 template <typename... KArgs, typename... Args>

@@ -495,10 +495,15 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
         }
         const int ch = chunk_of<G>(lu, r);
         if (active && (ch & 1) == 0) {  // one of the two lanes stores the block's byte
-          const __amdgpu_buffer_rsrc_t bsr = make_rsrc(bs, long(M) * (Kp / 32));
-          __builtin_amdgcn_raw_buffer_store_b8(uint8_t(eb), bsr,
-                                               uint32_t(m * (Kp / 32) + j * (G / 32) + (ch >> 2)),
-                                               0, 0);
+          // Scale rows are padded to whole dwords (4 ceil(K'/128) bytes); the lane of the
+          // row's last block also writes the (zero) padding bytes.
+          const int srow = ((Kp + 127) >> 7) * 4;
+          const __amdgpu_buffer_rsrc_t bsr = make_rsrc(bs, long(M) * srow);
+          const int gb = j * (G / 32) + (ch >> 2);
+          __builtin_amdgcn_raw_buffer_store_b8(uint8_t(eb), bsr, uint32_t(m * srow + gb), 0, 0);
+          if (gb == (Kp >> 5) - 1)
+            for (int pb = gb + 1; pb < srow; ++pb)
+              __builtin_amdgcn_raw_buffer_store_b8(uint8_t(0), bsr, uint32_t(m * srow + pb), 0, 0);
         }
       }
     } else {
@@ -673,7 +678,7 @@ hipError_t launch_plan(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t 
   }
   if (p.waves > MW || ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   // MXFP4 block-scale bytes are addressed with 32-bit offsets from bs.
-  if (FMT == kFmtMx4 && M * (Kp / 32) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (FMT == kFmtMx4 && M * ((Kp + 127) / 128 * 4) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int nblocks = int((M + p.R - 1) / p.R);
   const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)), fmt_bits<FMT>(),
                                 FMT != kFmtMx4);

@@ -186,6 +186,8 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(
 namespace big {
 
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -203,6 +205,16 @@ constexpr int kDmaA = kBM / 16, kDmaB = kBN / 16;  // 1 KB (16 rows x 64 B) tran
 constexpr int kDma = kDmaA + kDmaB;                // 32 per stage
 constexpr int kDmaPerWave = kDma / kWaves;
 constexpr uint32_t kOob = 0x80000000u;
+
+// Code formats (QB): 4 = packed int4, 8 = int8, kQbMx = MXFP4 (packed E2M1 codes, like int4,
+// plus one E8M0 byte per 32 codes).  MXFP4 stages also hold each row's four scale bytes of
+// the step (A rows then B rows, one dword per row), moved by one extra 256-byte transfer per
+// wave, and accumulate in fp32 on v_mfma_scale_f32_32x32x64_f8f6f4.
+constexpr int kQbMx = 1;
+constexpr int kScaleStage = 4 * (kBM + kBN);
+template <int QB> constexpr int code_bits() { return QB == 8 ? 8 : 4; }
+template <int QB> constexpr int stage_bytes() { return kStage + (QB == kQbMx ? kScaleStage : 0); }
+template <int QB> constexpr int dma_per_wave() { return kDmaPerWave + (QB == kQbMx ? 1 : 0); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -232,10 +244,24 @@ __device__ __forceinline__ uint32_t transfer_offset(int g, int lane, int rowB, i
 // This wave's transfers of one stage (A groups wave, wave + kWaves, ...; then B groups).
 // A and B address their LDS region from the stage base without selects, so the compiler
 // can tell the stages apart and keep the newer transfers in flight.
+template <int QB>
 __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t ra,
-                                            __amdgpu_buffer_rsrc_t rb, int rowB, int step,
-                                            int wave, int lane) {
+                                            __amdgpu_buffer_rsrc_t rb,
+                                            __amdgpu_buffer_rsrc_t rsa,
+                                            __amdgpu_buffer_rsrc_t rsb, int rowB, int srow,
+                                            int step, int wave, int lane) {
   const int kb = step * kBKB;
+  if constexpr (QB == kQbMx) {
+    // scale dwords of rows 64 t .. 64 t + 63 (t = wave % 4): A for waves 0-3, B for 4-7
+    const int t = wave & 3;
+    const uint32_t off = 4 * step < srow ? uint32_t((64 * t + lane) * srow + 4 * step) : kOob;
+    if (wave < 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(st + kStage + 256 * t), 4, off, 0,
+                                               0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr)(st + kStage + 4 * kBM + 256 * t),
+                                               4, off, 0, 0, 0);
+  }
 #pragma unroll
   for (int i = 0; i < kDmaA / kWaves; ++i) {
     const int g = wave + kWaves * i;
@@ -256,8 +282,11 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t 
 // feeding MFMA substeps 2c and 2c + 1; int8: chunk 2c + h, feeding substep c.  Weights and
 // activations use the same mapping, so the K order seen by the MFMA is the same on both
 // sides and the sums are unchanged.
+// MXFP4 uses the int8 mapping (a 32-byte slice per MFMA) and, with chunk 0, reads its rows'
+// scale dwords shifted right by 8 h, so that byte 2 c is the scale of the lane's block.
 struct Half {
   uint4 w[kGN], x[kGM];
+  uint32_t sw[kGN], sx[kGM];
 };
 
 template <int QB>
@@ -265,6 +294,14 @@ __device__ __forceinline__ void read_half(const uint8_t* st, int c, int wn, int 
                                           Half& f) {
   const int r32 = lane & 31, h = lane >> 5;
   const int q = QB == 4 ? 2 * h + c : 2 * c + h;
+  if (QB == kQbMx && c == 0) {
+    const uint32_t* SA = reinterpret_cast<const uint32_t*>(st + kStage);
+    const uint32_t* SB = SA + kBM;
+#pragma unroll
+    for (int j = 0; j < kGM; ++j) f.sx[j] = SA[wm * kTM + 32 * j + r32] >> (8 * h);
+#pragma unroll
+    for (int i = 0; i < kGN; ++i) f.sw[i] = SB[wn * kTN + 32 * i + r32] >> (8 * h);
+  }
   const uint4* A = reinterpret_cast<const uint4*>(st);
   const uint4* B = reinterpret_cast<const uint4*>(st + kAStage);
 #pragma unroll
@@ -279,9 +316,24 @@ __device__ __forceinline__ v4i unpack_half(const uint4 v, int s) {
   return v4i{int((a << 4) & m), int(a & m), int((b << 4) & m), int(b & m)};
 }
 
-// The MFMA substeps of one chunk: two (int4, after unpacking) or one (int8, as loaded).
-template <int QB>
-__device__ __forceinline__ void mma_half(const Half& f, v16i (&acc)[kGN][kGM]) {
+// The MFMA substeps of chunk C: two (int4, after unpacking) or one (int8 and MXFP4, as
+// loaded; MXFP4 takes its block scales from fs, the stage's chunk-0 fragments).
+template <int QB, int C>
+__device__ __forceinline__ void mma_half(const Half& f, const Half& fs, v16i (&acc)[kGN][kGM]) {
+  if constexpr (QB == kQbMx) {
+#pragma unroll
+    for (int i = 0; i < kGN; ++i)
+#pragma unroll
+      for (int j = 0; j < kGM; ++j) {
+        const v8i a = {int(f.w[i].x), int(f.w[i].y), int(f.w[i].z), int(f.w[i].w), 0, 0, 0, 0};
+        const v8i b = {int(f.x[j].x), int(f.x[j].y), int(f.x[j].z), int(f.x[j].w), 0, 0, 0, 0};
+        acc[i][j] = __builtin_bit_cast(
+            v16i, __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                      a, b, __builtin_bit_cast(v16f, acc[i][j]), 4, 4, 2 * C, fs.sw[i], 2 * C,
+                      fs.sx[j]));
+      }
+    return;
+  }
   if constexpr (QB == 8) {
 #pragma unroll
     for (int i = 0; i < kGN; ++i)
@@ -336,9 +388,14 @@ __device__ __forceinline__ void epi_block(const v16i (&acc)[kGN][kGM], int j, fl
       int32_t t[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
-        t[r] = QB == 4 ? acc[i][j][4 * g + r] >> 8 : acc[i][j][4 * g + r];
-        z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]), bv[r]);
+        if constexpr (QB == kQbMx) {  // fp32 sums, block scales already applied
+          t[r] = acc[i][j][4 * g + r];
+          z[r] = __fadd_rn(__int_as_float(t[r]), bv[r]);
+        } else {
+          // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
+          t[r] = QB == 4 ? acc[i][j][4 * g + r] >> 8 : acc[i][j][4 * g + r];
+          z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]), bv[r]);
+        }
       }
       if (kDbg && mrow + r32 < M) {  // raw integer sums, for verification only
         const long n = n0 + wn * kTN + c;
@@ -417,11 +474,12 @@ __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
                        const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+                       const uint8_t* __restrict__ xbs, const uint8_t* __restrict__ wbs,
                        const uint16_t* __restrict__ bias, int M, int N, int Kp,
                        int tiles_m, int tiles_n, uint16_t* __restrict__ y,
                        int32_t* __restrict__ acc_dbg) {
-  __shared__ __attribute__((aligned(16))) uint8_t st0[kStage], st1[kStage], st2[kStage],
-      st3[kStage];
+  constexpr int kSt = stage_bytes<QB>(), kDpw = dma_per_wave<QB>();
+  __shared__ __attribute__((aligned(16))) uint8_t st0[kSt], st1[kSt], st2[kSt], st3[kSt];
 
   // XCD-grouped tile order: blocks are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous range of tiles, walked four tile-rows at a time.
@@ -445,7 +503,8 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
   int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   asm volatile("" : "+s"(wave));
   const int wn = wave & 1, wm = wave >> 1;
-  const int rowB = Kp * QB / 8;  // bytes of codes per row
+  const int rowB = Kp * code_bits<QB>() / 8;  // bytes of codes per row
+  const int srow = ((Kp + 127) >> 7) * 4;       // MXFP4: bytes of block scales per row
   const int nsteps = (rowB + kBKB - 1) / kBKB;
   // Epilogue factors, loaded now so their latency hides behind the K loop.
   float xsv, wsv;
@@ -454,12 +513,16 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
     const int tid = wave * 64 + lane;  // one row and one column of the tile per thread
     const long mx = m0 + tid, nx = n0 + tid;
     const bool own = tid < kBM;
-    xsv = own && mx < M ? xs[mx] : 0.f;
-    wsv = own && nx < N ? ws[nx] : 0.f;
+    xsv = QB != kQbMx && own && mx < M ? xs[mx] : 0.f;
+    wsv = QB != kQbMx && own && nx < N ? ws[nx] : 0.f;
     bbits = (own && bias != nullptr && nx < N) ? uint32_t(bias[nx]) : 0x8000u;
   }
   const __amdgpu_buffer_rsrc_t ra = rsrc(xq + m0 * rowB, (long(M) - m0) * rowB);
   const __amdgpu_buffer_rsrc_t rb = rsrc(wq + n0 * rowB, (long(N) - n0) * rowB);
+  const __amdgpu_buffer_rsrc_t rsa =
+      rsrc(QB == kQbMx ? xbs + m0 * srow : xq, QB == kQbMx ? (long(M) - m0) * srow : 0);
+  const __amdgpu_buffer_rsrc_t rsb =
+      rsrc(QB == kQbMx ? wbs + n0 * srow : wq, QB == kQbMx ? (long(N) - n0) * srow : 0);
 
   v16i acc[kGN][kGM];
 #pragma unroll
@@ -479,21 +542,21 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
   // transfers.)  The loop is unrolled by four so every buffer is named statically, which
   // lets the compiler keep the newer transfers in flight.
   Half f0, f1, g0;
-  issue_stage(st0, ra, rb, rowB, 0, wave, lane);
-  issue_stage(st1, ra, rb, rowB, 1, wave, lane);
-  issue_stage(st2, ra, rb, rowB, 2, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDmaPerWave));  // vmcnt: stage 0 landed
+  issue_stage<QB>(st0, ra, rb, rsa, rsb, rowB, srow, 0, wave, lane);
+  issue_stage<QB>(st1, ra, rb, rsa, rsb, rowB, srow, 1, wave, lane);
+  issue_stage<QB>(st2, ra, rb, rsa, rsb, rowB, srow, 2, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDpw));  // vmcnt: stage 0 landed
   __builtin_amdgcn_s_barrier();
   read_half<QB>(st0, 0, wn, wm, lane, f0);
 #define CONVROT_STEP(K, CUR, NEXT, REFILL)                                          \
-  __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerWave); /* vmcnt: stage K + 1 landed */  \
+  __builtin_amdgcn_s_waitcnt(0x0F70 | kDpw);        /* vmcnt: stage K + 1 landed */  \
   __builtin_amdgcn_s_waitcnt(0xC07F);               /* lgkmcnt(0) */                \
   __builtin_amdgcn_s_barrier();                                                     \
-  issue_stage(REFILL, ra, rb, rowB, (K) + 3, wave, lane);                           \
+  issue_stage<QB>(REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);       \
   read_half<QB>(CUR, 1, wn, wm, lane, f1);                                          \
   read_half<QB>(NEXT, 0, wn, wm, lane, g0);                                         \
-  mma_half<QB>(f0, acc);                                                            \
-  mma_half<QB>(f1, acc);                                                            \
+  mma_half<QB, 0>(f0, f0, acc);                                                     \
+  mma_half<QB, 1>(f1, f0, acc);                                                     \
   f0 = g0;
   int k = 0;
   for (; k + 4 <= nsteps; k += 4) {
@@ -737,16 +800,19 @@ hipError_t launch_skinny(const uint8_t* xq, const float* xs, const uint8_t* wq, 
 template <int QB>
 hipError_t launch_big(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                       const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
-                      int32_t* acc_dbg, hipStream_t stream) {
+                      int32_t* acc_dbg, hipStream_t stream, const uint8_t* xbs = nullptr,
+                      const uint8_t* wbs = nullptr) {
   const int tiles_m = int((M + big::kBM - 1) / big::kBM);
   const int tiles_n = int((N + big::kBN - 1) / big::kBN);
   const int T = tiles_m * tiles_n;
   const dim3 grid(unsigned(8 * ((T + 7) / 8))), block(big::kThreads);
   if (acc_dbg != nullptr)
     return launch_kernel(big::quant_gemm_kernel<true, QB>, grid, block, 0, stream, xq, xs, wq,
-                         ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
+                         ws, xbs, wbs, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y,
+                         acc_dbg);
   return launch_kernel(big::quant_gemm_kernel<false, QB>, grid, block, 0, stream, xq, xs, wq,
-                       ws, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y, acc_dbg);
+                       ws, xbs, wbs, bias, int(M), int(N), int(Kp), tiles_m, tiles_n, y,
+                       acc_dbg);
 }
 
 }  // namespace
@@ -789,6 +855,14 @@ hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
   if (M <= kSkinnyMaxM8)
     return launch_skinny<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   return launch_big<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+}
+
+hipError_t launch_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_t* wq,
+                             const uint8_t* wbs, const uint16_t* bias, int64_t M, int64_t N,
+                             int64_t Kp, uint16_t* y, float* acc_dbg, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  return launch_big<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y,
+                                reinterpret_cast<int32_t*>(acc_dbg), stream, xbs, wbs);
 }
 
 }  // namespace convrot

@@ -48,8 +48,11 @@ def _announce(msg):
 def check_mx(gpu_q, gpu_bs, gpu_rot, ref, label="", max_frac=CODE_MISMATCH_MAX):
     yf = ref["yf"].astype(np.float64)
     rows, kp = yf.shape
-    bs = gpu_bs.cpu().numpy()
-    assert bs.dtype == np.uint8 and bs.shape == ref["scales"].shape
+    bs_all = gpu_bs.cpu().numpy()
+    nb = ref["scales"].shape[1]
+    assert bs_all.dtype == np.uint8 and bs_all.shape == (rows, 4 * (-(-kp // 128)))
+    assert np.all(bs_all[:, nb:] == 0), f"{label}: scale padding not zero"
+    bs = bs_all[:, :nb]
     db = bs.astype(np.int64) - ref["scales"].astype(np.int64)
     bad = np.nonzero(db)
     if len(bad[0]):
@@ -92,7 +95,7 @@ ROTATE_CASES = [
     (7, 200, 64, "f32"), (130, 1000, 64, "bf16"), (200, 3072, 256, "bf16"),
     (37, 3100, 256, "bf16"), (33, 777, 256, "f32"), (48, 12288, 1024, "bf16"),
     (23, 3000, 1024, "bf16"), (3, 61440, 1024, "bf16"), (2, 32768, 1024, "f32"),
-    (2, 32768, 64, "bf16"),
+    (2, 32768, 64, "bf16"), (9, 3000, 64, "bf16"), (5, 190, 64, "f32"),
 ]
 
 
@@ -145,3 +148,98 @@ def test_mxfp4_weights_and_strides(cr):
 def test_mxfp4_rejects_group_16(cr):
     with pytest.raises(cr.ConvRotError):
         cr.convrot_rotate_quant_act_mxfp4(torch.zeros((2, 64), dtype=torch.bfloat16, device=DEV), 16)
+
+
+def _pad_scales(e8, kp):
+    out = np.zeros((e8.shape[0], 4 * (-(-kp // 128))), dtype=np.uint8)
+    out[:, : e8.shape[1]] = e8
+    return out
+
+
+def check_mx_gemm(y, acc, ref, kp, bias, label=""):
+    """fp32 sums within the accumulation bound; the bf16 output exactly the epilogue of the
+    GPU's own sums; nearly all outputs bit-identical to the oracle's."""
+    a = acc.cpu().numpy().astype(np.float64)
+    bound = (kp / 64 + 2) * 2.0 ** -23 * ref["abs_sum"] + 1e-30
+    err = np.abs(a - ref["sum"])
+    assert np.all(err <= bound), f"{label}: sum error {np.max(err / bound):.2f} x the bound"
+    z = acc.cpu().numpy().astype(np.float32)
+    if bias is not None:
+        z = (z + bias[None, :].astype(np.float32)).astype(np.float32)
+    ybits = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(ybits, O.f32_to_bf16_bits(z)), f"{label}: epilogue differs"
+    same = np.mean(ybits == ref["out_bits"])
+    assert same >= 0.99, f"{label}: only {same:.4f} of the outputs match the oracle's bits"
+
+
+MX_GEMM_CASES = [
+    # M, N, Kp, bias
+    (1, 1, 64, False), (64, 64, 192, True), (300, 500, 320, True), (129, 257, 1088, False),
+    (1000, 2200, 3008, True), (4608, 3072, 256, True), (200, 300, 12288, False),
+]
+
+
+@pytest.mark.parametrize("M,N,Kp,with_bias", MX_GEMM_CASES)
+def test_mxfp4_gemm_parity(cr, M, N, Kp, with_bias):
+    _announce(f"mxfp4 gemm M={M} N={N} Kp={Kp} bias={with_bias}")
+    rng = np.random.default_rng(M + 5 * N + Kp)
+    cx = rng.integers(0, 16, size=(M, Kp)).astype(np.uint8)
+    cw = rng.integers(0, 16, size=(N, Kp)).astype(np.uint8)
+    ex = rng.integers(112, 142, size=(M, Kp // 32)).astype(np.uint8)
+    ew = rng.integers(112, 142, size=(N, Kp // 32)).astype(np.uint8)
+    b = wk.round_to_dtype(rng.standard_normal(N).astype(np.float32), "bf16") if with_bias else None
+    ref = O.mxfp4_linear_from_codes(cx, ex, cw, ew, b)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    bias = None if b is None else torch.from_numpy(b).to(torch.bfloat16).to(DEV)
+    args = (dev(O.pack_int4(cx)), dev(_pad_scales(ex, Kp)), dev(O.pack_int4(cw)),
+            dev(_pad_scales(ew, Kp)), bias)
+    y, acc = cr.convrot_mxfp4_gemm(*args, want_acc=True)
+    y2 = cr.convrot_mxfp4_gemm(*args)
+    torch.cuda.synchronize()
+    check_mx_gemm(y, acc, ref, Kp, b, f"M={M} N={N} Kp={Kp}")
+    assert torch.equal(y, y2), "the production instantiation differs from the debug one"
+
+
+MX_LINEAR_CASES = [
+    # M, K, N, g, dtype, bias
+    (64, 256, 256, 64, "f32", False), (200, 3072, 320, 256, "bf16", True),
+    (130, 3100, 200, 256, "bf16", False), (70, 12288, 136, 1024, "bf16", False),
+    (33, 1000, 130, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("M,K,N,g,dtype,with_bias", MX_LINEAR_CASES)
+def test_mxfp4_linear_parity(cr, M, K, N, g, dtype, with_bias):
+    _announce(f"mxfp4 linear M={M} K={K} N={N} g={g} {dtype} bias={with_bias}")
+    wl = wk.custom("t", M, K, N, g, x_dtype=dtype, bias_std=0.01 if with_bias else None)
+    x, w, b = wk.activations(wl), wk.weights(wl), wk.bias(wl)
+    ref = O.convlinear_fp4(x, w, b, g)
+    wq, wbs = cr.convrot_quant_weight_mxfp4(_to_dev(w, dtype), g)
+    bias = None if b is None else _to_dev(b, "bf16")
+    y = cr.convrot_mxfp4_linear(_to_dev(x, dtype), g, wq, wbs, bias)
+    xq, xbs = cr.convrot_rotate_quant_act_mxfp4(_to_dev(x, dtype), g)
+    torch.cuda.synchronize()
+    check_mx(wq, wbs, None, ref["w"], "weights")
+    check_mx(xq, xbs, None, ref["x"], "activations")
+    yo = O.bf16_bits_to_f32(ref["out_bits"]).astype(np.float64)
+    frob = np.linalg.norm(y.float().cpu().numpy() - yo) / max(np.linalg.norm(yo), 1e-30)
+    assert frob <= 1e-2, f"rel Frobenius {frob:.2e}"
+    # given the GPU's own codes, the output is the GEMM of those codes
+    kp = O.padded_k(K, g)
+    nb = kp // 32
+    cx = O.unpack_int4(xq.cpu().numpy()) & 0xF
+    cw = O.unpack_int4(wq.cpu().numpy()) & 0xF
+    own = O.mxfp4_linear_from_codes(cx, xbs.cpu().numpy()[:, :nb], cw, wbs.cpu().numpy()[:, :nb], b)
+    ybits = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.mean(ybits == own["out_bits"]) >= 0.99
+
+
+def test_mxfp4_empty_and_errors(cr):
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
+    wq = torch.zeros((8, 128), dtype=torch.uint8, device=DEV)
+    wbs = torch.zeros((8, 8), dtype=torch.uint8, device=DEV)
+    assert cr.convrot_mxfp4_linear(x, 256, wq, wbs).shape == (0, 8)
+    with pytest.raises(cr.ConvRotError):
+        cr.convrot_mxfp4_linear(torch.zeros((2, 64), dtype=torch.bfloat16, device=DEV), 16,
+                                torch.zeros((8, 32), dtype=torch.uint8, device=DEV),
+                                torch.zeros((8, 4), dtype=torch.uint8, device=DEV))
