@@ -15,7 +15,9 @@ launches of that kernel.  The CPU oracle is timed over whole passes of the same 
 (`cpu_baseline`).
 
 `--codes int8` measures the W8A8 variant the same way (convrot_rotate_quant_act_i8 and
-convrot_w8a8_gemm, the kernels convrot_w8a8_linear enqueues) and prints its own line.
+convrot_w8a8_gemm, the kernels convrot_w8a8_linear enqueues) and prints its own line;
+`--codes mxfp4` the MXFP4 variant (convrot_rotate_quant_act_mxfp4 and convrot_mxfp4_gemm),
+its GEMM against the FP4 matrix peak (10.1 PFLOP/s).
 """
 from __future__ import annotations
 
@@ -31,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W4A4 linear TOPS + rotate-quant GB/s (% of roofline) at M=4608,K=3072,g=256"
 METRIC_W8A8 = "W8A8 linear TOPS + rotate-quant GB/s (% of roofline) at M=4608,K=3072,g=256"
+METRIC_MXFP4 = "MXFP4 linear TOPS + rotate-quant GB/s (% of roofline) at M=4608,K=3072,g=256"
+FP4_PEAK_TOPS = 10100.0         # MI355X dense FP4 matrix throughput (10.1 PFLOP/s)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 matrix throughput (5.0 POP/s)
 MALL_BYTES = 256 << 20          # Infinity Cache; rotate inputs through > 2x this
@@ -42,8 +46,9 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="attn_proj")
-    p.add_argument("--codes", choices=("int4", "int8"), default="int4",
-                   help="int4: the W4A4 layer (default); int8: the W8A8 variant")
+    p.add_argument("--codes", choices=("int4", "int8", "mxfp4"), default="int4",
+                   help="int4: the W4A4 layer (default); int8: the W8A8 variant; mxfp4: the "
+                        "floating-point 4-bit variant")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = all)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -99,9 +104,12 @@ def gpu_bench(args, wl):
     w = torch.from_numpy(wkmod.weights(wl)).to(tdt).to(dev)
     b = wkmod.bias(wl)
     bias = None if b is None else torch.from_numpy(b).to(torch.bfloat16).to(dev)
-    i8 = args.codes == "int8"
+    i8, mx = args.codes == "int8", args.codes == "mxfp4"
     qbytes = Kp if i8 else Kp // 2              # code bytes per row
-    wq, ws = (cr.convrot_quant_weight_i8 if i8 else cr.convrot_quant_weight)(w, g)
+    sbytes = cr.mx_scale_stride(Kp) if mx else 4  # scale bytes per row
+    quant_w = (cr.convrot_quant_weight_i8 if i8 else
+               cr.convrot_quant_weight_mxfp4 if mx else cr.convrot_quant_weight)
+    wq, ws = quant_w(w, g)
     # With few activation rows the GEMM streams the weights: rotate them through copies too,
     # so that they come from HBM rather than from the Infinity Cache.
     w_bytes = wq.numel() * wq.element_size()
@@ -110,7 +118,8 @@ def gpu_bench(args, wl):
     n_y = 4
     ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(n_y)]
     xq = torch.empty((M, qbytes), dtype=torch.uint8, device=dev)
-    xsc = torch.empty((M,), dtype=torch.float32, device=dev)
+    xsc = (torch.empty((M, sbytes), dtype=torch.uint8, device=dev) if mx else
+           torch.empty((M,), dtype=torch.float32, device=dev))
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -121,6 +130,8 @@ def gpu_bench(args, wl):
     rq, gemm = lib.convrot_rotate_quant_act, lib.convrot_w4a4_gemm
     if i8:
         rq, gemm = lib.convrot_rotate_quant_act_i8, lib.convrot_w8a8_gemm
+    if mx:  # the same arguments, block scales in place of row scales
+        rq, gemm = lib.convrot_rotate_quant_act_mxfp4, lib.convrot_mxfp4_gemm
     xq_p, xs_p, ws_p = xq.data_ptr(), xsc.data_ptr(), ws.data_ptr()
     wq_ptrs = [t.data_ptr() for t in wq_list]
 
@@ -182,13 +193,14 @@ def gpu_bench(args, wl):
 
     ms_step = (t1 - t0) * 1e3 / K_steps
     ops = 2.0 * M * N * Kp
-    rq_bytes = M * K * x0.element_size() + M * qbytes + 4 * M
+    rq_bytes = M * K * x0.element_size() + M * qbytes + M * sbytes
     rq_us = float(np.mean(rq_ms) * 1e3)
     gemm_us = float(np.mean(gemm_ms) * 1e3)
     rq_gbps = rq_bytes / (rq_us * 1e-6) / 1e9
     gemm_tops = ops / (gemm_us * 1e-6) / 1e12
     # GEMM algorithmic bytes: code operands once, scales, bias, bf16 output
-    gemm_bytes = M * qbytes + N * qbytes + 4 * (M + N) + (2 * N if bias is not None else 0) + 2 * M * N
+    gemm_bytes = ((M + N) * (qbytes + sbytes) + (2 * N if bias is not None else 0)
+                  + 2 * M * N)
     return {
         "ms_per_step": ms_step, "ms_per_step_events": step_ms_events,
         "value": ops / (ms_step * 1e-3) / 1e12,
@@ -211,15 +223,20 @@ def cpu_baseline(args, wl):
     x = wkmod.activations(wl)
     w = wkmod.weights(wl)
     b = wkmod.bias(wl)
-    i8 = args.codes == "int8"
-    refw = (O.quantize_weight_int8 if i8 else O.quantize_weight)(w, wl.g)   # offline, untimed
+    i8, mx = args.codes == "int8", args.codes == "mxfp4"
+    quant = (O.rotate_quantize_int8 if i8 else O.rotate_quantize_mxfp4 if mx else
+             O.rotate_quantize)
+    refw = quant(w, wl.g)                                                   # offline, untimed
     rows = args.cpu_rows or wl.M
     xs = x[:rows]
     passes, t0 = 0, time.perf_counter()
     while True:
-        r = (O.rotate_quantize_int8 if i8 else O.rotate_quantize)(xs, wl.g)
-        lin = O.w8a8_linear_from_codes if i8 else O.w4a4_linear_from_codes
-        lin(r["codes"], r["scale"], refw["codes"], refw["scale"], b)
+        r = quant(xs, wl.g)
+        if mx:
+            O.mxfp4_linear_from_codes(r["codes"], r["scales"], refw["codes"], refw["scales"], b)
+        else:
+            lin = O.w8a8_linear_from_codes if i8 else O.w4a4_linear_from_codes
+            lin(r["codes"], r["scale"], refw["codes"], refw["scale"], b)
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= args.cpu_seconds or passes >= 100:
@@ -256,28 +273,31 @@ def main():
     r = gpu_bench(args, wl)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl)
     from rotation_w4a4_quantized_convrot_amd import profiling
-    i8 = args.codes == "int8"
+    i8, mx = args.codes == "int8", args.codes == "mxfp4"
     # which GEMM kernel the library picks for this shape (see w4a4_gemm.hip)
     rows16 = i8 or (wl.Kp // 2) % 16 == 0
-    if rows16 and wl.M <= (256 if i8 else 512):
+    if mx:
+        gemm_kernel, big = "mxfp4_gemm", True
+    elif rows16 and wl.M <= (256 if i8 else 512):
         gemm_kernel, big = "skinny_gemm", False
     elif i8 or (rows16 and wl.M * wl.N >= (1 << 21) and wl.M >= 128):
         gemm_kernel, big = ("w8a8_gemm" if i8 else "w4a4_gemm"), True
     else:
         gemm_kernel, big = "w4a4_gemm_kernel", False
-    rq_kernel = "rht_quant_i8" if i8 else "rht_quant_i4"
+    rq_kernel = "rht_quant_i8" if i8 else "rht_quant_mx4" if mx else "rht_quant_i4"
+    mfma_peak = FP4_PEAK_TOPS if mx else INT8_PEAK_TOPS
     traffic_file = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     # the recorded counters are for the attention-projection workload's launches
     profiled = wl.name == "attn_proj"
     tg = profiling.read_traffic(traffic_file, gemm_kernel) if big and profiled else None
     tq = profiling.read_traffic(traffic_file, rq_kernel) if profiled else None
     # The GEMM's binding roof: matrix cores, unless its bytes take longer at the HBM peak
-    # than its operations at the int8 peak (few activation rows).
-    if r["gemm_bytes"] / (HBM_PEAK_GBPS * 1e9) > r["gemm_ops"] / (INT8_PEAK_TOPS * 1e12):
+    # than its operations at the matrix peak of its code type (few activation rows).
+    if r["gemm_bytes"] / (HBM_PEAK_GBPS * 1e9) > r["gemm_ops"] / (mfma_peak * 1e12):
         roof = {"bound": "hbm", "achieved": r["gemm_bytes"] / (r["gemm_us"] * 1e-6) / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": r["gemm_tops"], "peak": INT8_PEAK_TOPS,
+        roof = {"bound": "mfma", "achieved": r["gemm_tops"], "peak": mfma_peak,
                 "unit": "TFLOP/s"}
     roof.update({"frac": roof["achieved"] / roof["peak"],
                  "traffic": None if tg is None else tg["fetch_bytes"] + tg["write_bytes"],
@@ -292,9 +312,10 @@ def main():
                "launch_us_median": r["rq_us_median"],
                "algorithmic_bytes_per_launch": r["rq_bytes"]}
     out = {
-        "metric": METRIC_W8A8 if i8 else METRIC, "value": r["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC_W8A8 if i8 else METRIC_MXFP4 if mx else METRIC, "value": r["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "i8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp4" if mx else "i8",
+        "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "g": wl.g, "Kp": wl.Kp,
                    "x_dtype": wl.x_dtype, "bias": wl.bias_std is not None,
                    "x_buffers": r["x_buffers"], "w_buffers": r["w_buffers"]},

@@ -32,8 +32,10 @@ CALIBRATION_BYTES = 256 << 20          # bench.py --copy-calibration: bytes read
 KERNELS = {
     "w4a4_gemm": ("quant_gemm_kernel<false, 4>", "w4a4_gemm.hip"),
     "w8a8_gemm": ("quant_gemm_kernel<false, 8>", "w4a4_gemm.hip"),
-    "rht_quant_i4": ("rht_quant_kernel<256, unsigned short, 16, 4>", "rht_quant.hip"),
-    "rht_quant_i8": ("rht_quant_kernel<256, unsigned short, 16, 8>", "rht_quant.hip"),
+    "rht_quant_i4": ("rht_quant_kernel<256, unsigned short, 16, 4", "rht_quant.hip"),
+    "rht_quant_i8": ("rht_quant_kernel<256, unsigned short, 16, 8", "rht_quant.hip"),
+    "rht_quant_mx4": ("rht_quant_kernel<256, unsigned short, 16, 1", "rht_quant.hip"),
+    "mxfp4_gemm": ("quant_gemm_kernel<false, 1>", "w4a4_gemm.hip"),
 }
 
 
