@@ -276,11 +276,12 @@ __device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t rs, uint32_t e
   }
 }
 
+// Row-internal DPP permutations give every lane a source, so no fallback value is needed.
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0, uint32_t(b), CTRL, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0, uint32_t(b >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = __builtin_amdgcn_mov_dpp(int(uint32_t(b)), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp(int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, false);
   return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
 }
 
@@ -293,14 +294,20 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 
 // Exact |fp32(y[p])| of position p of a window whose raw inputs (bf16 or fp32, in position
 // order, zero past column K) sit in LDS at win, computed by the whole wavefront in fp64:
-// sum_t (-1)^(#equal base-4 digits of p and t) x[t], times 2^-k.  Lane l sums T consecutive
-// positions; the 16 lanes of a row are combined with DPP and the four rows through readlane.
-// The fp64 sums are exact for bf16 windows whose exponent spread is below 35 binades.
+// sum_t (-1)^(#equal base-4 digits of p and t) x[t], times 2^-k.  Lane l sums the T
+// consecutive positions t = T l + i.  The low base-4 digits of t are those of i, so their
+// share of the sign depends only on i and p (uniform across the wave); the high digits are
+// those of l, one sign per lane.  The 16 lanes of a row are combined with DPP and the four
+// rows through readlane.  The fp64 sums are exact for bf16 windows whose exponent spread is
+// below 35 binades.
 template <int G, typename TIn>
 __device__ __forceinline__ float exact_rotated_abs(const TIn* win, int p, int lane) {
   constexpr int KD = Geo<G>::KD;
-  constexpr int kDigitMask = 0x55555 & ((1 << (2 * KD)) - 1);
-  constexpr int T = (G + 63) / 64;   // consecutive positions per lane
+  constexpr int T = (G + 63) / 64;   // consecutive positions per lane: 1, 1, 4 or 16
+  constexpr int KL = T == 16 ? 2 : T == 4 ? 1 : 0;  // base-4 digits of i
+  constexpr int kLoMask = 0x5 & ((1 << (2 * KL)) - 1);
+  constexpr int kHiMask = 0x55555 & ((1 << (2 * (KD - KL))) - 1);
+  const int plo = p & (T - 1), phi = p >> (2 * KL);
   double acc = 0.0;
   if (lane * T < G) {
     float xv[T];
@@ -327,11 +334,16 @@ __device__ __forceinline__ float exact_rotated_abs(const TIn* win, int p, int la
       for (int i = 0; i < T; ++i) xv[i] = reinterpret_cast<const float*>(win)[lane * T + i];
     }
 #pragma unroll
-    for (int i = 0; i < T; ++i) {
-      const int d = p ^ (lane * T + i);
-      const int differing = __builtin_popcount((d | (d >> 1)) & kDigitMask);
-      acc += ((KD - differing) & 1) ? -(double)xv[i] : (double)xv[i];
+    for (int i = 0; i < T; ++i) {  // the sign of a term flips its top bit (uniform mask)
+      const int d = i ^ plo;
+      const int equal_lo = KL - __builtin_popcount((d | (d >> 1)) & kLoMask);
+      const double t = __builtin_bit_cast(
+          double, __builtin_bit_cast(uint64_t, (double)xv[i]) ^ (uint64_t(equal_lo & 1) << 63));
+      acc = i == 0 ? t : acc + t;
     }
+    const int d = lane ^ phi;
+    const int equal_hi = (KD - KL) - __builtin_popcount((d | (d >> 1)) & kHiMask);
+    if (equal_hi & 1) acc = -acc;
   }
   acc += dpp_f64<kDppXor1>(acc);
   acc += dpp_f64<kDppXor2>(acc);
@@ -589,17 +601,14 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       uint64_t cand = __ballot(live && cm[r] >= thr);
+      if (cand == 0) continue;
+      uint32_t m8 = 0;  // this lane's candidate elements of chunk r
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m8 |= uint32_t(fabsf(v[8 * r + e]) >= thr) << e;
       while (cand) {  // lanes whose chunk r holds a candidate
         const int src = __builtin_ctzll(cand);
         cand &= cand - 1;
-        const float s_thr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(thr), src));
-        uint32_t elems = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a =
-              fabsf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[8 * r + e]), src)));
-          elems |= uint32_t(a >= s_thr) << e;
-        }
+        uint32_t elems = __builtin_amdgcn_readlane(m8, src);
         const int s_unit = src / L;
         const int s_rloc = __builtin_amdgcn_readlane(rloc, src), s_lu = src % L;
         const int p0 = 8 * chunk_of<G>(s_lu, r);
