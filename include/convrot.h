@@ -232,8 +232,9 @@ CONVROT_API int convrot_quant_weight_mxfp4(const void* w, int32_t w_dtype, int64
  *   bytes, S = 4 ceil(Kp/128) (4-byte aligned); bias bf16 [N] or NULL; y bf16 [M][N] (4-byte
  *   aligned); Kp a positive multiple of 64, <= CONVROT_MAX_KP; acc_dbg fp32 [M][N] (16-byte
  *   aligned) receives the sums before the bias, or NULL.
- * The order in which the hardware adds the products is not specified: the sum carries fp32
- * rounding of at most about Kp/64 roundings of partial sums, not an exact result.
+ * The order in which the products are added is not specified: the sum carries fp32 rounding
+ * of at most about Kp/64 + 16 roundings of partial sums, not an exact result (for M <= 256 the
+ * K range is split over up to 16 waves whose partial sums are added last).
  * M = 0 or N = 0 is a no-op.  Errors: SHAPE, NULL, ALIGN, UNSUPPORTED, HIP. */
 CONVROT_API int convrot_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_t* wq,
                                    const uint8_t* wbs, const void* bias, int64_t M, int64_t N,

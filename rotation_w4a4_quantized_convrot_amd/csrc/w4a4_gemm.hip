@@ -594,8 +594,9 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
 // into MFMA registers (each weight byte is read from HBM once; the activation codes, shared
 // by every workgroup, come from L2) through a ring of kDepth K steps in flight per wave, and
 // the partial sums meet in LDS (64 KB).  The dequantization factors are fetched before the
-// K loop so that their latency overlaps it.  The chunk-to-lane mapping and the int4
-// unpacking are those of the tiled kernel.
+// K loop so that their latency overlaps it.  The chunk-to-lane mapping, the int4 unpacking
+// and the MXFP4 scale handling are those of the tiled kernel.  MXFP4 partial sums are fp32,
+// added in wave order, so the skinny kernel's rounding differs from the tiled kernel's.
 namespace skinny {
 
 using big::v16i;
@@ -616,17 +617,26 @@ __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int row, int byt
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, int row, int byte, int rowB) {
+  const uint32_t off = byte < rowB ? uint32_t(row * rowB + byte) : big::kOob;
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
 // One K step of this lane's operands: chunks c = 0, 1 of its weight row and of its row in
-// each 32-row activation block.
+// each 32-row activation block; for MXFP4 also the four block-scale bytes of the step of
+// those rows (one dword per row, shifted right by 8 h so that byte 2 c is the scale of the
+// lane's 32-code block, as in the tiled kernel).
 template <int MB>
 struct Frag {
   uint4 w[2], x[MB][2];
+  uint32_t sw, sx[MB];
 };
 
 template <int QB, int MB>
 __device__ __forceinline__ void load_step(Frag<MB>& f, __amdgpu_buffer_rsrc_t rw,
-                                          __amdgpu_buffer_rsrc_t rx, int step, int rowB,
-                                          int lane) {
+                                          __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsw,
+                                          __amdgpu_buffer_rsrc_t rsx, int step, int rowB,
+                                          int srow, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
@@ -636,10 +646,36 @@ __device__ __forceinline__ void load_step(Frag<MB>& f, __amdgpu_buffer_rsrc_t rw
 #pragma unroll
     for (int j = 0; j < MB; ++j) f.x[j][c] = ld16(rx, 32 * j + r32, byte, rowB);
   }
+  if constexpr (QB == big::kQbMx) {
+    f.sw = ld4(rsw, r32, 4 * step, srow) >> (8 * h);
+#pragma unroll
+    for (int j = 0; j < MB; ++j) f.sx[j] = ld4(rsx, 32 * j + r32, 4 * step, srow) >> (8 * h);
+  }
+}
+
+// MXFP4 chunk C: fp32 sums, the block scales applied by the instruction (byte 2 C of the
+// shifted scale dwords).
+template <int C, int MB>
+__device__ __forceinline__ void mma_mx(const Frag<MB>& f, v16i (&acc)[MB]) {
+  const big::v8i a = {int(f.w[C].x), int(f.w[C].y), int(f.w[C].z), int(f.w[C].w), 0, 0, 0, 0};
+#pragma unroll
+  for (int j = 0; j < MB; ++j) {
+    const big::v8i b = {int(f.x[j][C].x), int(f.x[j][C].y), int(f.x[j][C].z), int(f.x[j][C].w),
+                        0, 0, 0, 0};
+    acc[j] = __builtin_bit_cast(
+        v16i, __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  a, b, __builtin_bit_cast(big::v16f, acc[j]), 4, 4, 2 * C, f.sw, 2 * C,
+                  f.sx[j]));
+  }
 }
 
 template <int QB, int MB>
 __device__ __forceinline__ void mma_step(const Frag<MB>& f, v16i (&acc)[MB]) {
+  if constexpr (QB == big::kQbMx) {
+    mma_mx<0, MB>(f, acc);
+    mma_mx<1, MB>(f, acc);
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     if constexpr (QB == 8) {
@@ -661,22 +697,29 @@ __device__ __forceinline__ void mma_step(const Frag<MB>& f, v16i (&acc)[MB]) {
   }
 }
 
+// QB: 4 (packed int4), 8 (int8) or big::kQbMx (MXFP4: packed E2M1 codes with E8M0 block
+// scales in xbs / wbs, fp32 sums; the partial sums of the waves are added in wave order).
 template <bool kDbg, int QB, int MB>
 __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
-    const float* __restrict__ ws, const uint16_t* __restrict__ bias, int M, int N, int Kp,
+    const float* __restrict__ ws, const uint8_t* __restrict__ xbs,
+    const uint8_t* __restrict__ wbs, const uint16_t* __restrict__ bias, int M, int N, int Kp,
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg) {
+  constexpr bool kMx = QB == big::kQbMx;
   constexpr int kWaves = Shape<MB>::kWaves, kThreads = Shape<MB>::kThreads;
   constexpr int kDepth = Shape<MB>::kDepth, kGroups = Shape<MB>::kGroups;
   __shared__ int32_t red[kWaves * MB * 16 * 64];  // 64 KB: every wave's partial sums
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long n0 = (long)blockIdx.x * kTN, m0 = (long)blockIdx.y * (32 * MB);
-  const int rowB = Kp * QB / 8;  // bytes of codes per row
+  const int rowB = Kp * big::code_bits<QB>() / 8;  // bytes of codes per row
+  const int srow = ((Kp + 127) >> 7) * 4;           // MXFP4: bytes of block scales per row
+  const long nw = min(long(N) - n0, long(kTN)), mx = min(long(M) - m0, long(32 * MB));
   // Rows past the tile (or past N, M) read as zero through the buffer range check.
-  const __amdgpu_buffer_rsrc_t rw = big::rsrc(wq + n0 * rowB, min(long(N) - n0, long(kTN)) * rowB);
-  const __amdgpu_buffer_rsrc_t rx =
-      big::rsrc(xq + m0 * rowB, min(long(M) - m0, long(32 * MB)) * rowB);
+  const __amdgpu_buffer_rsrc_t rw = big::rsrc(wq + n0 * rowB, nw * rowB);
+  const __amdgpu_buffer_rsrc_t rx = big::rsrc(xq + m0 * rowB, mx * rowB);
+  const __amdgpu_buffer_rsrc_t rsw = big::rsrc(kMx ? wbs + n0 * srow : wq, kMx ? nw * srow : 0);
+  const __amdgpu_buffer_rsrc_t rsx = big::rsrc(kMx ? xbs + m0 * srow : xq, kMx ? mx * srow : 0);
   const int nsteps = (rowB + kStepB - 1) / kStepB;
   const int per = (nsteps + kWaves - 1) / kWaves;
   const int k0 = min(nsteps, wave * per), k1 = min(nsteps, k0 + per);
@@ -687,7 +730,7 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
   Frag<MB> f[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
-    if (k0 + d < k1) load_step<QB, MB>(f[d], rw, rx, k0 + d, rowB, lane);
+    if (k0 + d < k1) load_step<QB, MB>(f[d], rw, rx, rsw, rsx, k0 + d, rowB, srow, lane);
 
   // Dequantization factors of this thread's output groups (four consecutive columns of one
   // row each; see below), fetched now so that the loads overlap the K loop.
@@ -698,11 +741,11 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
     const int l = gi & 63, g = (gi >> 6) & 3, j = gi >> 8;
     const long m = m0 + 32 * j + (l & 31), n = n0 + 8 * g + 4 * (l >> 5);
     const bool live = gi < MB * 256 && m < M;
-    fsx[i] = live ? xs[m] : 0.f;
+    fsx[i] = !kMx && live ? xs[m] : 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool in = live && n + r < N;
-      fw[i][r] = in ? ws[n + r] : 0.f;
+      fw[i][r] = !kMx && in ? ws[n + r] : 0.f;
       // bf16 -> fp32 is exact; a missing bias is -0.0, an exact identity for the add
       fb[i][r] = (in && bias != nullptr) ? __uint_as_float(uint32_t(bias[n + r]) << 16) : -0.0f;
     }
@@ -713,7 +756,8 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
     for (int d = 0; d < kDepth; ++d) {
       if (k + d < k1) {
         mma_step<QB, MB>(f[d], acc);
-        if (k + d + kDepth < k1) load_step<QB, MB>(f[d], rw, rx, k + d + kDepth, rowB, lane);
+        if (k + d + kDepth < k1)
+          load_step<QB, MB>(f[d], rw, rx, rsw, rsx, k + d + kDepth, rowB, srow, lane);
       }
     }
   }
@@ -739,12 +783,21 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
     int32_t t[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      int32_t a = 0;
+      if constexpr (kMx) {
+        float a = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) a += red[((w * MB + j) * 16 + 4 * g + r) * 64 + l];
-      // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
-      t[r] = QB == 4 ? a >> 8 : a;
-      z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], fsx[i]), fw[i][r]), fb[i][r]);
+        for (int w = 0; w < kWaves; ++w)
+          a = __fadd_rn(a, __int_as_float(red[((w * MB + j) * 16 + 4 * g + r) * 64 + l]));
+        t[r] = __float_as_int(a);
+        z[r] = __fadd_rn(a, fb[i][r]);
+      } else {
+        int32_t a = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) a += red[((w * MB + j) * 16 + 4 * g + r) * 64 + l];
+        // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
+        t[r] = QB == 4 ? a >> 8 : a;
+        z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], fsx[i]), fw[i][r]), fb[i][r]);
+      }
     }
     const bf16x2 lo = __builtin_convertvector((f32x2){z[0], z[1]}, bf16x2);
     const bf16x2 hi = __builtin_convertvector((f32x2){z[2], z[3]}, bf16x2);
@@ -773,28 +826,33 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
 
 template <int QB, int MB>
 hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* wq,
-                            const float* ws, const uint16_t* bias, int64_t M, int64_t N,
-                            int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
+                            const float* ws, const uint8_t* xbs, const uint8_t* wbs,
+                            const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
+                            int32_t* acc_dbg, hipStream_t stream) {
   const dim3 grid(unsigned((N + skinny::kTN - 1) / skinny::kTN), unsigned((M + 32 * MB - 1) / (32 * MB)));
   const dim3 block(skinny::Shape<MB>::kThreads);
   if (acc_dbg != nullptr)
     return launch_kernel(skinny::quant_gemm_skinny_kernel<true, QB, MB>, grid, block, 0, stream,
-                         xq, xs, wq, ws, bias, int(M), int(N), int(Kp), y, acc_dbg);
+                         xq, xs, wq, ws, xbs, wbs, bias, int(M), int(N), int(Kp), y, acc_dbg);
   return launch_kernel(skinny::quant_gemm_skinny_kernel<false, QB, MB>, grid, block, 0, stream, xq,
-                       xs, wq, ws, bias, int(M), int(N), int(Kp), y, acc_dbg);
+                       xs, wq, ws, xbs, wbs, bias, int(M), int(N), int(Kp), y, acc_dbg);
 }
 
-// Largest M routed to the skinny kernel, per code width.
-constexpr int64_t kSkinnyMaxM4 = 512, kSkinnyMaxM8 = 256;
+// Largest M routed to the skinny kernel, per code format (measured on MI355X at N = K' = 3072:
+// int4 and MXFP4 against the tiled kernel of the same format).
+constexpr int64_t kSkinnyMaxM4 = 512, kSkinnyMaxM8 = 256, kSkinnyMaxMx = 256;
 
 // Activation rows per skinny workgroup: 32, 64 or 128.
 template <int QB>
 hipError_t launch_skinny(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                          const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
-                         int32_t* acc_dbg, hipStream_t stream) {
-  if (M <= 32) return launch_skinny_mb<QB, 1>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-  if (M <= 64) return launch_skinny_mb<QB, 2>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-  return launch_skinny_mb<QB, 4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+                         int32_t* acc_dbg, hipStream_t stream, const uint8_t* xbs = nullptr,
+                         const uint8_t* wbs = nullptr) {
+  if (M <= 32)
+    return launch_skinny_mb<QB, 1>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
+  if (M <= 64)
+    return launch_skinny_mb<QB, 2>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
+  return launch_skinny_mb<QB, 4>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
 }
 
 template <int QB>
@@ -861,8 +919,17 @@ hipError_t launch_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_
                              const uint8_t* wbs, const uint16_t* bias, int64_t M, int64_t N,
                              int64_t Kp, uint16_t* y, float* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  return launch_big<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y,
-                                reinterpret_cast<int32_t*>(acc_dbg), stream, xbs, wbs);
+  int32_t* dbg = reinterpret_cast<int32_t*>(acc_dbg);
+#ifdef CONVROT_GEMM_PATH
+  if (CONVROT_GEMM_PATH == 1)
+    return launch_skinny<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream,
+                                     xbs, wbs);
+#endif
+  if (M <= kSkinnyMaxMx)
+    return launch_skinny<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream,
+                                     xbs, wbs);
+  return launch_big<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream, xbs,
+                                wbs);
 }
 
 }  // namespace convrot

@@ -160,7 +160,9 @@ def check_mx_gemm(y, acc, ref, kp, bias, label=""):
     """fp32 sums within the accumulation bound; the bf16 output exactly the epilogue of the
     GPU's own sums; nearly all outputs bit-identical to the oracle's."""
     a = acc.cpu().numpy().astype(np.float64)
-    bound = (kp / 64 + 2) * 2.0 ** -23 * ref["abs_sum"] + 1e-30
+    # one rounding per 64-code instruction, plus the skinny kernel's sum of up to 16 per-wave
+    # partial sums (the order of the fp32 additions is the implementation's)
+    bound = (kp / 64 + 18) * 2.0 ** -23 * ref["abs_sum"] + 1e-30
     err = np.abs(a - ref["sum"])
     assert np.all(err <= bound), f"{label}: sum error {np.max(err / bound):.2f} x the bound"
     z = acc.cpu().numpy().astype(np.float32)
@@ -174,8 +176,12 @@ def check_mx_gemm(y, acc, ref, kp, bias, label=""):
 
 MX_GEMM_CASES = [
     # M, N, Kp, bias
-    (1, 1, 64, False), (64, 64, 192, True), (300, 500, 320, True), (129, 257, 1088, False),
-    (1000, 2200, 3008, True), (4608, 3072, 256, True), (200, 300, 12288, False),
+    # M <= 256: the skinny kernel (32, 64 or 128 activation rows per workgroup)
+    (1, 1, 64, False), (64, 64, 192, True), (129, 257, 1088, False), (200, 300, 12288, False),
+    (33, 100, 1024, True), (40, 70, 64, False), (256, 96, 256, False),
+    # the tiled kernel
+    (257, 64, 128, True), (300, 500, 320, True), (1000, 2200, 3008, True),
+    (4608, 3072, 256, True),
 ]
 
 
