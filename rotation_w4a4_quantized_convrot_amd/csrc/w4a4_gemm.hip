@@ -612,13 +612,16 @@ struct Shape {
   static constexpr int kGroups = (MB * 256 + kThreads - 1) / kThreads;  // outputs / 4 / thread
 };
 
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int row, int byte, int rowB) {
-  const uint32_t off = byte < rowB ? uint32_t(row * rowB + byte) : big::kOob;
+// 16 bytes at byte `byte` of row `row` (row stride rowB); bytes at or past lim read zero.
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int row, int byte, int lim,
+                                      int rowB) {
+  const uint32_t off = byte < lim ? uint32_t(row * rowB + byte) : big::kOob;
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, int row, int byte, int rowB) {
-  const uint32_t off = byte < rowB ? uint32_t(row * rowB + byte) : big::kOob;
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, int row, int byte, int lim,
+                                        int rowB) {
+  const uint32_t off = byte < lim ? uint32_t(row * rowB + byte) : big::kOob;
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
@@ -632,24 +635,28 @@ struct Frag {
   uint32_t sw, sx[MB];
 };
 
+// A step that is not this wave's (valid false) reads zeros without touching memory, so that
+// every wave issues the same loads and the compiler can count them exactly.
 template <int QB, int MB>
 __device__ __forceinline__ void load_step(Frag<MB>& f, __amdgpu_buffer_rsrc_t rw,
                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsw,
-                                          __amdgpu_buffer_rsrc_t rsx, int step, int rowB,
-                                          int srow, int lane) {
+                                          __amdgpu_buffer_rsrc_t rsx, int step, bool valid,
+                                          int rowB, int srow, int lane) {
   const int r32 = lane & 31, h = lane >> 5;
+  const int lim = valid ? rowB : 0, slim = valid ? srow : 0;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int q = QB == 4 ? 2 * h + c : 2 * c + h;
     const int byte = step * kStepB + 16 * q;
-    f.w[c] = ld16(rw, r32, byte, rowB);
+    f.w[c] = ld16(rw, r32, byte, lim, rowB);
 #pragma unroll
-    for (int j = 0; j < MB; ++j) f.x[j][c] = ld16(rx, 32 * j + r32, byte, rowB);
+    for (int j = 0; j < MB; ++j) f.x[j][c] = ld16(rx, 32 * j + r32, byte, lim, rowB);
   }
   if constexpr (QB == big::kQbMx) {
-    f.sw = ld4(rsw, r32, 4 * step, srow) >> (8 * h);
+    f.sw = ld4(rsw, r32, 4 * step, slim, srow) >> (8 * h);
 #pragma unroll
-    for (int j = 0; j < MB; ++j) f.sx[j] = ld4(rsx, 32 * j + r32, 4 * step, srow) >> (8 * h);
+    for (int j = 0; j < MB; ++j)
+      f.sx[j] = ld4(rsx, 32 * j + r32, 4 * step, slim, srow) >> (8 * h);
   }
 }
 
@@ -727,37 +734,61 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
   v16i acc[MB];
 #pragma unroll
   for (int j = 0; j < MB; ++j) acc[j] = v16i{};
-  Frag<MB> f[kDepth];
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (k0 + d < k1) load_step<QB, MB>(f[d], rw, rx, rsw, rsx, k0 + d, rowB, srow, lane);
-
   // Dequantization factors of this thread's output groups (four consecutive columns of one
-  // row each; see below), fetched now so that the loads overlap the K loop.
-  float fsx[kGroups], fw[kGroups][4], fb[kGroups][4];
+  // row each; see below), requested first and used only by the epilogue, so that their
+  // latency overlaps the K loop: unconditional buffer loads (offsets out of range read
+  // zero), the bias kept as raw bf16 bits until the epilogue.
+  const __amdgpu_buffer_rsrc_t rxs = big::rsrc(kMx ? nullptr : xs, kMx ? 0 : long(M) * 4);
+  const __amdgpu_buffer_rsrc_t rws = big::rsrc(kMx ? nullptr : ws, kMx ? 0 : long(N) * 4);
+  const __amdgpu_buffer_rsrc_t rbs = big::rsrc(bias, bias != nullptr ? long(N) * 2 : 0);
+  float fsx[kGroups], fw[kGroups][4];
+  uint32_t fb[kGroups][4];
 #pragma unroll
   for (int i = 0; i < kGroups; ++i) {
     const int gi = tid + kThreads * i;
     const int l = gi & 63, g = (gi >> 6) & 3, j = gi >> 8;
     const long m = m0 + 32 * j + (l & 31), n = n0 + 8 * g + 4 * (l >> 5);
     const bool live = gi < MB * 256 && m < M;
-    fsx[i] = !kMx && live ? xs[m] : 0.f;
+    fsx[i] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rxs, live ? uint32_t(m * 4) : big::kOob, 0, 0));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool in = live && n + r < N;
-      fw[i][r] = !kMx && in ? ws[n + r] : 0.f;
-      // bf16 -> fp32 is exact; a missing bias is -0.0, an exact identity for the add
-      fb[i][r] = (in && bias != nullptr) ? __uint_as_float(uint32_t(bias[n + r]) << 16) : -0.0f;
+      fw[i][r] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rws, in ? uint32_t((n + r) * 4) : big::kOob,
+                                                      0, 0));
+      fb[i][r] = __builtin_bit_cast(
+          unsigned short, __builtin_amdgcn_raw_buffer_load_b16(
+                              rbs, in ? uint32_t((n + r) * 2) : big::kOob, 0, 0));
     }
+  }
+
+  // The ring of K steps.  With 128 activation rows (MB = 4, two steps in flight) it is
+  // branch-free: steps past this wave's range load zeros and add zeros, and scheduling
+  // barriers keep the loads in ring order, so that each wait is for the oldest step only
+  // (vector memory loads return in order).  With fewer rows a wave has only a few steps and
+  // loads exactly those; that measured faster there (M <= 64), the branch-free form faster
+  // at M >= 128.
+  constexpr bool kOrdered = MB == 4;
+  Frag<MB> f[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    if (kOrdered || k0 + d < k1)
+      load_step<QB, MB>(f[d], rw, rx, rsw, rsx, k0 + d, k0 + d < k1, rowB, srow, lane);
+    if constexpr (kOrdered) __builtin_amdgcn_sched_barrier(0);
   }
 
   for (int k = k0; k < k1; k += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      if (k + d < k1) {
+      const int kn = k + d + kDepth;
+      if constexpr (kOrdered) {
         mma_step<QB, MB>(f[d], acc);
-        if (k + d + kDepth < k1)
-          load_step<QB, MB>(f[d], rw, rx, rsw, rsx, k + d + kDepth, rowB, srow, lane);
+        load_step<QB, MB>(f[d], rw, rx, rsw, rsx, kn, kn < k1, rowB, srow, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if (k + d < k1) {
+        mma_step<QB, MB>(f[d], acc);
+        if (kn < k1) load_step<QB, MB>(f[d], rw, rx, rsw, rsx, kn, true, rowB, srow, lane);
       }
     }
   }
@@ -783,20 +814,22 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
     int32_t t[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      // bf16 -> fp32 is exact; a missing bias is -0.0, an exact identity for the add
+      const float bv = bias != nullptr ? __uint_as_float(fb[i][r] << 16) : -0.0f;
       if constexpr (kMx) {
         float a = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
           a = __fadd_rn(a, __int_as_float(red[((w * MB + j) * 16 + 4 * g + r) * 64 + l]));
         t[r] = __float_as_int(a);
-        z[r] = __fadd_rn(a, fb[i][r]);
+        z[r] = __fadd_rn(a, bv);
       } else {
         int32_t a = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) a += red[((w * MB + j) * 16 + 4 * g + r) * 64 + l];
         // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
         t[r] = QB == 4 ? a >> 8 : a;
-        z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], fsx[i]), fw[i][r]), fb[i][r]);
+        z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], fsx[i]), fw[i][r]), bv);
       }
     }
     const bf16x2 lo = __builtin_convertvector((f32x2){z[0], z[1]}, bf16x2);
