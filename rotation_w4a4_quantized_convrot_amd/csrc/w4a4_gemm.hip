@@ -914,10 +914,6 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const bool rows16 = (Kp / 2) % 16 == 0;  // 16-byte packed rows
-#ifdef CONVROT_GEMM_PATH
-  if (CONVROT_GEMM_PATH == 1 && rows16)
-    return launch_skinny<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-#endif
   // Few activation rows: 256 x 256 tiles would leave most CUs idle (measured on MI355X at
   // N = 3072: the skinny kernel is faster up to M = 512).
   if (rows16 && M <= kSkinnyMaxM4)
@@ -938,10 +934,6 @@ hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             const float* ws, const uint16_t* bias, int64_t M, int64_t N,
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-#ifdef CONVROT_GEMM_PATH
-  if (CONVROT_GEMM_PATH == 1)
-    return launch_skinny<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-#endif
   // int8 operands double the skinny kernel's bytes per MFMA: it wins up to M = 256.
   if (M <= kSkinnyMaxM8)
     return launch_skinny<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
@@ -953,11 +945,6 @@ hipError_t launch_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_
                              int64_t Kp, uint16_t* y, float* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   int32_t* dbg = reinterpret_cast<int32_t*>(acc_dbg);
-#ifdef CONVROT_GEMM_PATH
-  if (CONVROT_GEMM_PATH == 1)
-    return launch_skinny<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream,
-                                     xbs, wbs);
-#endif
   if (M <= kSkinnyMaxMx)
     return launch_skinny<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream,
                                      xbs, wbs);
