@@ -178,7 +178,7 @@ MX_GEMM_CASES = [
     # M, N, Kp, bias
     # M <= 256: the skinny kernel (32, 64 or 128 activation rows per workgroup)
     (1, 1, 64, False), (64, 64, 192, True), (129, 257, 1088, False), (200, 300, 12288, False),
-    (33, 100, 1024, True), (40, 70, 64, False), (256, 96, 256, False),
+    (33, 100, 1024, True), (40, 70, 64, False), (100, 90, 512, True), (256, 96, 256, False),
     # the tiled kernel
     (257, 64, 128, True), (300, 500, 320, True), (1000, 2200, 3008, True),
     (4608, 3072, 256, True),
