@@ -1,0 +1,108 @@
+"""Seeded random shapes through the whole layer, every code format (needs a gfx950 GPU).
+
+The shape grid of the other parity tests is hand-picked around tile and window boundaries;
+these cases draw M, K, N, g, the input dtype and the bias at random (fixed seed, so the list
+is the same on every run) and apply the same bars: weight and activation codes and scales
+against the oracle, the end-to-end output within 1e-2 relative Frobenius error, and the output
+equal to the GEMM of the GPU's own codes (bit for bit for the integer formats, >= 99% of the
+bf16 outputs for MXFP4, whose sums are fp32).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wk
+from oracle import convrot_oracle as O
+from tests.test_gpu_mxfp4 import check_mx
+from tests.test_gpu_parity import check_rotate_quant
+from tests.test_gpu_w8a8 import check_i8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+OUT_FROB_MAX = 1e-2
+
+
+def _cases(n_per_format=8, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for fmt in ("int4", "int8", "mxfp4"):
+        for _ in range(n_per_format):
+            g = int(rng.choice([64, 256, 1024] if fmt == "mxfp4" else [16, 64, 256, 1024]))
+            M = int(rng.integers(1, 700))
+            N = int(rng.integers(1, 600))
+            K = int(rng.integers(max(1, g // 2), 6000))
+            dtype = str(rng.choice(["bf16", "f32"]))
+            out.append((fmt, M, K, N, g, dtype, bool(rng.integers(0, 2))))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rotation_w4a4_quantized_convrot_amd as mod
+    mod.load_library()  # raises if the HIP library is missing: no fallback
+    return mod
+
+
+def _to_dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).to(DEV)
+
+
+@pytest.mark.parametrize("fmt,M,K,N,g,dtype,with_bias", CASES)
+def test_random_shape_layer(cr, fmt, M, K, N, g, dtype, with_bias):
+    print(f"\n[case] {fmt} layer M={M} K={K} N={N} g={g} {dtype} bias={with_bias}", flush=True)
+    wl = wk.custom("r", M, K, N, g, x_dtype=dtype, bias_std=0.01 if with_bias else None)
+    x, w, b = wk.activations(wl), wk.weights(wl), wk.bias(wl)
+    xd, wd = _to_dev(x, dtype), _to_dev(w, dtype)
+    bias = None if b is None else _to_dev(b, "bf16")
+    if fmt == "int4":
+        ref = O.convlinear4bit(x, w, b, g)
+        wq, ws = cr.convrot_quant_weight(wd, g)
+        xq, xs = cr.convrot_rotate_quant_act(xd, g)
+        y = cr.convrot_w4a4_linear(xd, g, wq, ws, bias)
+        torch.cuda.synchronize()
+        check_rotate_quant(wq, ws, None, ref["w"], "weights")
+        check_rotate_quant(xq, xs, None, ref["x"], "activations")
+        own = O.w4a4_linear_from_codes(O.unpack_int4(xq.cpu().numpy()), xs.cpu().numpy(),
+                                       O.unpack_int4(wq.cpu().numpy()), ws.cpu().numpy(), b)
+        own_min = 1.0
+    elif fmt == "int8":
+        ref = O.convlinear8bit(x, w, b, g)
+        wq, ws = cr.convrot_quant_weight_i8(wd, g)
+        xq, xs = cr.convrot_rotate_quant_act_i8(xd, g)
+        y = cr.convrot_w8a8_linear(xd, g, wq, ws, bias)
+        torch.cuda.synchronize()
+        check_i8(wq, ws, None, ref["w"], "weights")
+        check_i8(xq, xs, None, ref["x"], "activations")
+        own = O.w8a8_linear_from_codes(xq.cpu().numpy(), xs.cpu().numpy(), wq.cpu().numpy(),
+                                       ws.cpu().numpy(), b)
+        own_min = 1.0
+    else:
+        ref = O.convlinear_fp4(x, w, b, g)
+        wq, wbs = cr.convrot_quant_weight_mxfp4(wd, g)
+        xq, xbs = cr.convrot_rotate_quant_act_mxfp4(xd, g)
+        y = cr.convrot_mxfp4_linear(xd, g, wq, wbs, bias)
+        torch.cuda.synchronize()
+        check_mx(wq, wbs, None, ref["w"], "weights")
+        check_mx(xq, xbs, None, ref["x"], "activations")
+        nb = O.padded_k(K, g) // 32
+        own = O.mxfp4_linear_from_codes(O.unpack_int4(xq.cpu().numpy()) & 0xF,
+                                        xbs.cpu().numpy()[:, :nb],
+                                        O.unpack_int4(wq.cpu().numpy()) & 0xF,
+                                        wbs.cpu().numpy()[:, :nb], b)
+        own_min = 0.99
+    yo = O.bf16_bits_to_f32(ref["out_bits"]).astype(np.float64)
+    yg = y.float().cpu().numpy().astype(np.float64)
+    den = np.linalg.norm(yo)
+    frob = np.linalg.norm(yg - yo) / den if den > 0 else np.linalg.norm(yg)
+    assert frob <= OUT_FROB_MAX, f"rel Frobenius {frob:.2e}"
+    ybits = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.mean(ybits == own["out_bits"]) >= own_min, "output is not the GEMM of the GPU's codes"
