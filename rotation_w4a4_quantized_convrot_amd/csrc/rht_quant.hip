@@ -509,13 +509,16 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
         if (active && (ch & 1) == 0) {  // one of the two lanes stores the block's byte
           // Scale rows are padded to whole dwords (4 ceil(K'/128) bytes); the lane of the
           // row's last block also writes the (zero) padding bytes.
+          // The range starts at the block's first row, so the 32-bit offsets stay small.
           const int srow = ((Kp + 127) >> 7) * 4;
-          const __amdgpu_buffer_rsrc_t bsr = make_rsrc(bs, long(M) * srow);
+          const long row0 = long(b) * R;
+          const __amdgpu_buffer_rsrc_t bsr = make_rsrc(bs + row0 * srow, (long(M) - row0) * srow);
           const int gb = j * (G / 32) + (ch >> 2);
-          __builtin_amdgcn_raw_buffer_store_b8(uint8_t(eb), bsr, uint32_t(m * srow + gb), 0, 0);
+          const uint32_t ro = uint32_t(rloc * srow);
+          __builtin_amdgcn_raw_buffer_store_b8(uint8_t(eb), bsr, ro + gb, 0, 0);
           if (gb == (Kp >> 5) - 1)
             for (int pb = gb + 1; pb < srow; ++pb)
-              __builtin_amdgcn_raw_buffer_store_b8(uint8_t(0), bsr, uint32_t(m * srow + pb), 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b8(uint8_t(0), bsr, ro + pb, 0, 0);
         }
       }
     } else {
@@ -692,14 +695,14 @@ hipError_t launch_plan(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t 
                        uint8_t* q, float* s, uint8_t* bs, float* xrot, hipStream_t stream) {
   constexpr int L = Geo<G>::L, U = 64 / L;
   const int W = int(Kp / G);
-  // Byte offsets inside a block are 32-bit: keep R rows of stride ldx below 2 GiB.
-  while (p.R > 1 && int64_t(p.R) * ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) {
+  // Byte offsets inside a block are 32-bit (every block has its own 64-bit base): keep R rows
+  // of stride ldx below 2 GiB.  With one row per block the offsets stay below K' elements
+  // whatever the stride.
+  if (p.R > 1 && int64_t(p.R) * ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) {
     p.R = 1;
     p.waves = (W + U - 1) / U;
   }
-  if (p.waves > MW || ldx * int64_t(sizeof(TIn)) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  // MXFP4 block-scale bytes are addressed with 32-bit offsets from bs.
-  if (FMT == kFmtMx4 && M * ((Kp + 127) / 128 * 4) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (p.waves > MW) return hipErrorInvalidValue;
   const int nblocks = int((M + p.R - 1) / p.R);
   const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)), fmt_bits<FMT>(),
                                 FMT != kFmtMx4);

@@ -77,7 +77,9 @@ __global__ __launch_bounds__(256) void w4a4_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
-  const long m0 = (long)blockIdx.x * kBM, n0 = (long)blockIdx.y * kBN;
+  // One-dimensional grid (no per-dimension block-count limit): row tiles vary fastest.
+  const int tiles_m = (M + kBM - 1) / kBM;
+  const long m0 = long(blockIdx.x % tiles_m) * kBM, n0 = long(blockIdx.x / tiles_m) * kBN;
   const int rowB = Kp / 2;
   const int nsteps = (rowB + kBKB - 1) / kBKB;
 
@@ -737,10 +739,12 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
   // Dequantization factors of this thread's output groups (four consecutive columns of one
   // row each; see below), requested first and used only by the epilogue, so that their
   // latency overlaps the K loop: unconditional buffer loads (offsets out of range read
-  // zero), the bias kept as raw bf16 bits until the epilogue.
-  const __amdgpu_buffer_rsrc_t rxs = big::rsrc(kMx ? nullptr : xs, kMx ? 0 : long(M) * 4);
-  const __amdgpu_buffer_rsrc_t rws = big::rsrc(kMx ? nullptr : ws, kMx ? 0 : long(N) * 4);
-  const __amdgpu_buffer_rsrc_t rbs = big::rsrc(bias, bias != nullptr ? long(N) * 2 : 0);
+  // zero), the bias kept as raw bf16 bits until the epilogue.  Each range starts at this
+  // workgroup's first row or column, so the 32-bit offsets stay small for any M and N.
+  const __amdgpu_buffer_rsrc_t rxs = big::rsrc(kMx ? nullptr : xs + m0, kMx ? 0 : mx * 4);
+  const __amdgpu_buffer_rsrc_t rws = big::rsrc(kMx ? nullptr : ws + n0, kMx ? 0 : nw * 4);
+  const __amdgpu_buffer_rsrc_t rbs = big::rsrc(bias != nullptr ? bias + n0 : nullptr,
+                                               bias != nullptr ? nw * 2 : 0);
   float fsx[kGroups], fw[kGroups][4];
   uint32_t fb[kGroups][4];
 #pragma unroll
@@ -750,16 +754,17 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
     const long m = m0 + 32 * j + (l & 31), n = n0 + 8 * g + 4 * (l >> 5);
     const bool live = gi < MB * 256 && m < M;
     fsx[i] = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rxs, live ? uint32_t(m * 4) : big::kOob, 0, 0));
+        float, __builtin_amdgcn_raw_buffer_load_b32(rxs, live ? uint32_t((m - m0) * 4) : big::kOob,
+                                                    0, 0));
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool in = live && n + r < N;
       fw[i][r] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(rws, in ? uint32_t((n + r) * 4) : big::kOob,
+          float, __builtin_amdgcn_raw_buffer_load_b32(rws, in ? uint32_t((n - n0 + r) * 4) : big::kOob,
                                                       0, 0));
       fb[i][r] = __builtin_bit_cast(
           unsigned short, __builtin_amdgcn_raw_buffer_load_b16(
-                              rbs, in ? uint32_t((n + r) * 2) : big::kOob, 0, 0));
+                              rbs, in ? uint32_t((n - n0 + r) * 2) : big::kOob, 0, 0));
     }
   }
 
@@ -875,6 +880,16 @@ hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* w
 // int4 and MXFP4 against the tiled kernel of the same format).
 constexpr int64_t kSkinnyMaxM4 = 512, kSkinnyMaxM8 = 256, kSkinnyMaxMx = 256;
 
+// A dispatch counts its work-items in 32-bit fields.  The skinny grid has N / 32 workgroups
+// of up to 1024 threads, so it fits only below about N = 2^27; wider outputs take another
+// kernel (the tiled one spans 256 columns per 512 threads).
+bool skinny_fits(int64_t M, int64_t N) {
+  const int64_t threads = M <= 32 ? skinny::Shape<1>::kThreads
+                          : M <= 128 ? skinny::Shape<2>::kThreads
+                                     : skinny::Shape<4>::kThreads;
+  return (N + skinny::kTN - 1) / skinny::kTN * threads <= int64_t(UINT32_MAX);
+}
+
 // Activation rows per skinny workgroup: 32, 64 or 128.
 template <int QB>
 hipError_t launch_skinny(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
@@ -919,12 +934,13 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
   const bool rows16 = (Kp / 2) % 16 == 0;  // 16-byte packed rows
   // Few activation rows: 256 x 256 tiles would leave most CUs idle (measured on MI355X at
   // N = 3072: the skinny kernel is faster up to M = 512).
-  if (rows16 && M <= kSkinnyMaxM4)
+  if (rows16 && M <= kSkinnyMaxM4 && skinny_fits(M, N))
     return launch_skinny<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-  // The large tile needs 16-byte packed rows and enough work to fill the chip.
-  if (rows16 && M * N >= (int64_t(1) << 21) && M >= big::kBM / 2)
+  // The large tile needs 16-byte packed rows and enough work to fill the chip (or an output
+  // too wide for the skinny grid).
+  if (rows16 && ((M * N >= (int64_t(1) << 21) && M >= big::kBM / 2) || M <= kSkinnyMaxM4))
     return launch_big<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-  const dim3 grid(unsigned((M + kBM - 1) / kBM), unsigned((N + kBN - 1) / kBN));
+  const dim3 grid(unsigned(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN)));
   const dim3 block(256);
   if (vec_bytes == 16)
     return launch_kernel(w4a4_gemm_kernel<16>, grid, block, 0, stream, xq, xs, wq, ws, bias,
@@ -938,7 +954,7 @@ hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   // int8 operands double the skinny kernel's bytes per MFMA: it wins up to M = 256.
-  if (M <= kSkinnyMaxM8)
+  if (M <= kSkinnyMaxM8 && skinny_fits(M, N))
     return launch_skinny<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   return launch_big<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
 }
@@ -948,7 +964,7 @@ hipError_t launch_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_
                              int64_t Kp, uint16_t* y, float* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   int32_t* dbg = reinterpret_cast<int32_t*>(acc_dbg);
-  if (M <= kSkinnyMaxMx)
+  if (M <= kSkinnyMaxMx && skinny_fits(M, N))
     return launch_skinny<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream,
                                      xbs, wbs);
   return launch_big<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream, xbs,
