@@ -40,7 +40,9 @@
  *     of convrot_make_rht.  The library never allocates, frees or retains device memory
  *     and keeps no mutable global state; calls are re-entrant.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
- *     enqueued asynchronously on it; no call synchronises the device or the stream.
+ *     enqueued asynchronously on it; no call synchronises the device or the stream.  Every
+ *     call enqueues kernel launches only (no memset, copy or allocation), so calls may be
+ *     recorded by stream capture into a HIP graph and replayed.
  *   - Every call validates its arguments on the host first and returns a status; on error
  *     nothing is enqueued and no output is written.
  *   - Inputs must be finite; NaN or Inf inputs give unspecified codes and scales.
