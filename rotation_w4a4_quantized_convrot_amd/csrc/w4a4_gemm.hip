@@ -896,7 +896,10 @@ hipError_t launch_skinny(const uint8_t* xq, const float* xs, const uint8_t* wq, 
                          const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
                          int32_t* acc_dbg, hipStream_t stream, const uint8_t* xbs = nullptr,
                          const uint8_t* wbs = nullptr) {
-  if (M <= 32)
+  // 32-row workgroups up to M = 64: one or two row blocks of 16-wave workgroups (measured at
+  // N = K' = 3072, weights from HBM, M = 64: int4 6.1 against 7.9 us, int8 9.8 against
+  // 15.2 us, MXFP4 7.2 against 9.6 us for 64-row workgroups; at M = 96 three row blocks lose).
+  if (M <= 64)
     return launch_skinny_mb<QB, 1>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
   // 64-row workgroups up to M = 128: twice the workgroups of the 128-row form and half the
   // K steps per wave (measured at N = K' = 3072, M = 128: int4 7.8 against 11.6 us, int8

@@ -174,7 +174,7 @@ GEMM_CASES = [
     # M <= 512: the skinny kernel (32, 64 and 128-row workgroups, ragged M, N and K)
     (1, 40, 128, True), (128, 128, 128, False), (200, 136, 1024, True), (129, 130, 256, True),
     (300, 257, 3072, False), (64, 256, 3328, True), (33, 96, 12288, False),
-    (300, 7000, 3328, False), (512, 3072, 3072, True),
+    (300, 7000, 3328, False), (512, 3072, 3072, True), (65, 200, 512, True),
     # large-tile kernel (M N >= 2^21): ragged M and N, several tiles, K tails
     (600, 3500, 512, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
 ]

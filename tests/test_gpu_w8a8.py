@@ -119,7 +119,7 @@ GEMM_CASES = [
     # M, N, Kp, bias
     # M <= 256: the skinny kernel
     (1, 1, 16, False), (64, 64, 64, True), (100, 200, 512, True), (129, 257, 1040, False),
-    (256, 3000, 3072, True), (16, 3072, 12288, False),
+    (256, 3000, 3072, True), (16, 3072, 12288, False), (48, 300, 1040, True),
     # the tiled kernel
     (300, 500, 320, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
 ]
