@@ -37,8 +37,9 @@
  *
  * Memory and threading:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except the host buffer
- *     of convrot_make_rht.  The library never allocates, frees or retains device memory
- *     and keeps no mutable global state; calls are re-entrant.
+ *     of convrot_make_rht.  The library never allocates, frees or retains device memory.
+ *     Its only global state is a per-device cache of the compute-unit count (atomic);
+ *     calls are re-entrant and may come from several host threads.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
  *     enqueued asynchronously on it; no call synchronises the device or the stream.  Every
  *     call enqueues kernel launches only (no memset, copy or allocation), so calls may be

@@ -30,6 +30,7 @@
 #include "convrot_internal.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace convrot {
 namespace {
@@ -675,15 +676,21 @@ RqPlan plan_rows(int W, int U, int G, int esize, int qb, bool raw, int max_waves
   return small.R > 0 && small_eff >= 0.75 ? small : best;
 }
 
+// Compute units of the current device, cached per device.  Calls from several host threads
+// may fill an entry at once; they store the same value, and the entries are atomic.
 int device_cus() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
-  static int cached[64] = {0};
-  if (dev >= 0 && dev < 64 && cached[dev] > 0) return cached[dev];
+  static std::atomic<int> cached[64];
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  if (dev >= 0 && dev < 64) cached[dev] = n;
+  if (slot) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
