@@ -544,6 +544,7 @@ def pin_mx_block_scale(o):
     y = rng.standard_normal((5, 256)) * np.exp2(rng.integers(-20, 20, size=(5, 1)))
     y[2, 32:64] = 0.0
     e = o.mx_block_exponents(y)
+    assert e.shape == (5, 8), "one shared exponent per 32 values"
     blocks = np.abs(y.reshape(5, 8, 32)).max(axis=2)
     live = blocks > 0
     ratio = blocks[live] / np.exp2(e[live].astype(np.float64))

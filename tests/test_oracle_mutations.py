@@ -124,6 +124,11 @@ def _e2m1_no_negative_zero(t):
     return np.where(c == 8, 0, c).astype(np.uint8)
 
 
+def _mx_values_unscaled(codes, e8m0):
+    # decoded codes without their block scale
+    return O.e2m1_decode(codes)
+
+
 MUTATIONS = {
     "sylvester_base": ({"base_regular_hadamard": _sylvester_base}, ["pin_regular"]),
     "negated_base": ({"base_regular_hadamard": lambda: -_orig["base_regular_hadamard"]()},
@@ -150,6 +155,9 @@ MUTATIONS = {
     "e2m1_lost_sign_of_zero": ({"e2m1_encode": _e2m1_no_negative_zero}, ["pin_e2m1_format"]),
     "mx_emax_3": ({"E2M1_EMAX": 3}, ["pin_mx_block_scale", "pin_mxfp4_round_trip",
                                      "pin_mxfp4_end_to_end_closed_form"]),
+    "mx_block_16": ({"MX_BLOCK": 16}, ["pin_mx_block_scale"]),
+    "mx_values_unscaled": ({"mxfp4_values": _mx_values_unscaled},
+                           ["pin_mxfp4_gemm_brute_force", "pin_mxfp4_round_trip"]),
 }
 
 
