@@ -41,9 +41,15 @@ template <> struct Geo<64>   { static constexpr int KD = 3, L = 2,  E = 32; };
 template <> struct Geo<256>  { static constexpr int KD = 4, L = 8,  E = 32; };
 template <> struct Geo<1024> { static constexpr int KD = 5, L = 16, E = 64; };
 
-// Cache policy of the code stores: non-temporal (streaming), bit 1 of the buffer
-// instruction's cache-policy operand on gfx950.
-constexpr int kStreamStore = 2;
+// Cache policy of the code stores, per format.  Non-temporal (bit 1 of the buffer
+// instruction's cache-policy operand on gfx950) makes this kernel faster on its own; the
+// default policy leaves the codes in the caches for the GEMM that reads them next.  Measured
+// on attn_proj, this kernel alone / whole rotate+quantize + GEMM steps, non-temporal against
+// default: int4 10.1 / 47.5 against 10.6 / 47.5 us; int8 10.9 / 57.8-58.0 against
+// 11.8 / 55.3-55.6 us; MXFP4 8.9 / 42.2-43.9 against 9.2 / 40.9-42.7 us.
+constexpr int kNonTemporal = 2;
+template <int FMT>
+constexpr int code_store_policy() { return FMT == kFmtInt4 ? kNonTemporal : 0; }
 
 // DPP controls (gfx9 encoding): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
 constexpr int kDppXor1 = 0xB1;
@@ -579,13 +585,13 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
       if constexpr (kLaneBytes == 8) {
         __builtin_amdgcn_raw_buffer_store_b64(
             __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned,
-                               *reinterpret_cast<const uint2*>(src)), qs, qoff, 0, kStreamStore);
+                               *reinterpret_cast<const uint2*>(src)), qs, qoff, 0, code_store_policy<FMT>());
       } else {
 #pragma unroll
         for (int i = 0; i < kLaneBytes / 16; ++i)
           __builtin_amdgcn_raw_buffer_store_b128(
               __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned,
-                                 reinterpret_cast<const uint4*>(src)[i]), qs, qoff + 16 * i, 0, kStreamStore);
+                                 reinterpret_cast<const uint4*>(src)[i]), qs, qoff + 16 * i, 0, code_store_policy<FMT>());
       }
     }
     if (xrot != nullptr && active) {
