@@ -1,11 +1,12 @@
 """Seeded random shapes through the whole layer, every code format (needs a gfx950 GPU).
 
 The shape grid of the other parity tests is hand-picked around tile and window boundaries;
-these cases draw M, K, N, g, the input dtype and the bias at random (fixed seed, so the list
-is the same on every run) and apply the same bars: weight and activation codes and scales
-against the oracle, the end-to-end output within 1e-2 relative Frobenius error, and the output
-equal to the GEMM of the GPU's own codes (bit for bit for the integer formats, >= 99% of the
-bf16 outputs for MXFP4, whose sums are fp32).
+these cases draw M, K, N, g, the input dtype and the bias at random (fixed seeds, so the list
+is the same on every run; small shapes, and a few large enough for the tiled GEMM) and apply
+the same bars: weight and activation codes and scales against the oracle, the end-to-end
+output within 1e-2 relative Frobenius error, and the output equal to the GEMM of the GPU's
+own codes (bit for bit for the integer formats, >= 99% of the bf16 outputs for MXFP4, whose
+sums are fp32).
 """
 from __future__ import annotations
 
@@ -25,21 +26,23 @@ DEV = "cuda:0"
 OUT_FROB_MAX = 1e-2
 
 
-def _cases(n_per_format=8, seed=2024):
+def _cases(n_per_format=8, seed=2024, m_range=(1, 700), n_range=(1, 600), k_max=6000):
     rng = np.random.default_rng(seed)
     out = []
     for fmt in ("int4", "int8", "mxfp4"):
         for _ in range(n_per_format):
             g = int(rng.choice([64, 256, 1024] if fmt == "mxfp4" else [16, 64, 256, 1024]))
-            M = int(rng.integers(1, 700))
-            N = int(rng.integers(1, 600))
-            K = int(rng.integers(max(1, g // 2), 6000))
+            M = int(rng.integers(*m_range))
+            N = int(rng.integers(*n_range))
+            K = int(rng.integers(max(1, g // 2), k_max))
             dtype = str(rng.choice(["bf16", "f32"]))
             out.append((fmt, M, K, N, g, dtype, bool(rng.integers(0, 2))))
     return out
 
 
-CASES = _cases()
+# small shapes (skinny and 128 x 128 GEMMs), then shapes large enough for the tiled GEMM
+CASES = _cases() + _cases(n_per_format=2, seed=11, m_range=(128, 3000), n_range=(700, 3000),
+                          k_max=4000)
 
 
 @pytest.fixture(scope="module")
