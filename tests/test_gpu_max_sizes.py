@@ -8,7 +8,8 @@ and columns against the oracle:
     kernel), and with N = 2^27 - 32, the widest output the skinny grid takes;
   * rotate+quantize of M = 2^29 + 256 rows (K = g = 64, bf16) in every format; the MXFP4
     block-scale rows alone then span more than 2 GiB;
-  * rotate+quantize of rows 2 GiB apart (a strided view), in every format.
+  * rotate+quantize of rows 2 GiB apart (a strided view), in every format;
+  * every format's GEMM at the largest depth accepted, K' = 65536, with int8 sums of 2^30.
 Inputs are drawn on the device with torch's seeded generator; only the sampled rows and
 columns come back to the host.  The bars are those of the format's own parity tests.
 """
@@ -149,3 +150,53 @@ def test_rotate_quant_row_stride_past_2gib(cr):
     check_rotate_quant(q, s, None, O.rotate_quantize(xh, g), "int4")
     check_i8(q8, s8, None, O.rotate_quantize_int8(xh, g), "int8")
     check_mx(qm, bm, None, O.rotate_quantize_mxfp4(xh, g), "mxfp4")
+
+
+@pytest.mark.parametrize("M,N", [(40, 70), (1100, 2000)])
+@pytest.mark.parametrize("codes", ["int4", "int8", "mxfp4"])
+def test_gemm_max_depth(cr, codes, M, N):
+    """K' = CONVROT_MAX_KP (65536), the skinny and the tiled kernel.  Row 0 of both operands
+    holds the most negative code everywhere, so int8 sums reach 16384 K' = 2^30; the other
+    rows are random full-range codes."""
+    Kp = 65536
+    print(f"\n[case] {codes} gemm max depth M={M} N={N} Kp={Kp}", flush=True)
+    rng = np.random.default_rng(M + N)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)  # noqa: E731
+    b = rng.standard_normal(N).astype(np.float32)
+    b = O.bf16_bits_to_f32(O.f32_to_bf16_bits(b))
+    bias = dev(b).to(torch.bfloat16)
+    if codes == "int8":
+        cx = rng.integers(-128, 128, size=(M, Kp)).astype(np.int8)
+        cw = rng.integers(-128, 128, size=(N, Kp)).astype(np.int8)
+        cx[0], cw[0] = -128, -128
+        xq, wq = dev(cx), dev(cw)
+    else:
+        cx = rng.integers(-8, 8, size=(M, Kp)).astype(np.int8)
+        cw = rng.integers(-8, 8, size=(N, Kp)).astype(np.int8)
+        if codes == "mxfp4":
+            cx, cw = cx & 0xF, cw & 0xF  # E2M1 codes 0..15; 0xF is -6, the largest magnitude
+            cx[0], cw[0] = 0xF, 0xF
+        else:
+            cx[0], cw[0] = -8, -8
+        xq, wq = dev(O.pack_int4(cx)), dev(O.pack_int4(cw))
+    if codes == "mxfp4":
+        S = cr.mx_scale_stride(Kp)
+        ex = rng.integers(118, 136, size=(M, S)).astype(np.uint8)
+        ew = rng.integers(118, 136, size=(N, S)).astype(np.uint8)
+        y, acc = cr.convrot_mxfp4_gemm(xq, dev(ex), wq, dev(ew), bias, want_acc=True)
+        torch.cuda.synchronize()
+        nb = Kp // 32
+        ref = O.mxfp4_linear_from_codes(cx.astype(np.uint8), ex[:, :nb], cw.astype(np.uint8),
+                                        ew[:, :nb], b)
+        check_mx_gemm(y, acc, ref, Kp, b, f"M={M} N={N}")
+        return
+    sx = (rng.random(M) * 1e-3 + 1e-5).astype(np.float32)
+    sw = (rng.random(N) * 1e-3 + 1e-5).astype(np.float32)
+    gemm = cr.convrot_w4a4_gemm if codes == "int4" else cr.convrot_w8a8_gemm
+    y, acc = gemm(xq, dev(sx), wq, dev(sw), bias, want_acc=True)
+    torch.cuda.synchronize()
+    ref = O.w8a8_linear_from_codes(cx, sx, cw, sw, b)
+    a = acc.cpu().numpy()
+    assert a[0, 0] == (16384 if codes == "int8" else 64) * Kp
+    assert np.array_equal(a, ref["acc"]), "int32 sums differ"
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref["out_bits"])
