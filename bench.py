@@ -264,7 +264,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by rows with no communication; see DESIGN.md).", file=sys.stderr)
+              "(rows are independent: the path would shard by rows, with no communication).", file=sys.stderr)
         sys.exit(2)
     import workloads as wkmod
     wl = wkmod.WORKLOADS[args.workload]

@@ -32,7 +32,7 @@ Sources (the web pages this follows, cited by title and section):
             accumulate x @ w^T in fp32 (exact integers), multiply by the
             per-row x scale and per-column w scale, add the bias, cast last.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * base matrix H4 = J4 - 2 I4 (symmetric; every row and column sums to +2);
     H_g = H4 (x) ... (x) H4 (k = log4 g factors); rotation = H_g / sqrt(g).
   * windows start at column 0; K is zero-padded to K' = ceil(K/g) g and the

@@ -1,6 +1,6 @@
 """HIP path vs the CPU oracle, element by element, through the C ABI (needs a gfx950 GPU).
 
-Bars (from the benchmark spec's tolerances, defined precisely here):
+Bars (the stated tolerances, defined precisely here):
   * scales: bit-identical to the oracle's fp32(exact absmax / 7);
   * codes: differ only by one and only at fp32 near-ties of the quotient, in at most 1e-4
     of all codes (at least one code may differ: a small array can hold a single tie);
