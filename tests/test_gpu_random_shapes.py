@@ -3,10 +3,12 @@
 The shape grid of the other parity tests is hand-picked around tile and window boundaries;
 these cases draw M, K, N, g, the input dtype and the bias at random (fixed seeds, so the list
 is the same on every run; small shapes, and a few large enough for the tiled GEMM) and apply
-the same bars: weight and activation codes and scales against the oracle, the end-to-end
-output within 1e-2 relative Frobenius error, and the output equal to the GEMM of the GPU's
-own codes (bit for bit for the integer formats, >= 99% of the bf16 outputs for MXFP4, whose
-sums are fp32).
+the same bars: weight and activation codes and scales against the oracle, the output equal
+to the GEMM of the GPU's own codes (bit for bit for the integer formats, >= 99% of the bf16
+outputs for MXFP4, whose sums are fp32), and the end-to-end output within 1e-2 relative
+Frobenius error of the oracle's.  A near-tie code may take either neighbour, and in a small
+output one such code can move the result by more than 1e-2: the bar then holds against the
+oracle's GEMM of the same codes.
 """
 from __future__ import annotations
 
@@ -42,7 +44,11 @@ def _cases(n_per_format=8, seed=2024, m_range=(1, 700), n_range=(1, 600), k_max=
 
 # small shapes (skinny and 128 x 128 GEMMs), then shapes large enough for the tiled GEMM
 CASES = _cases() + _cases(n_per_format=2, seed=11, m_range=(128, 3000), n_range=(700, 3000),
-                          k_max=4000)
+                          k_max=4000) + [
+    # found by a wider sweep: one activation code at a near-tie (quotient -0.4999997) moves
+    # this 23 x 86 output by 1.05e-2 from the oracle's
+    ("int4", 23, 787, 86, 1024, "f32", False),
+]
 
 
 @pytest.fixture(scope="module")
@@ -102,10 +108,36 @@ def test_random_shape_layer(cr, fmt, M, K, N, g, dtype, with_bias):
                                         O.unpack_int4(wq.cpu().numpy()) & 0xF,
                                         wbs.cpu().numpy()[:, :nb], b)
         own_min = 0.99
-    yo = O.bf16_bits_to_f32(ref["out_bits"]).astype(np.float64)
-    yg = y.float().cpu().numpy().astype(np.float64)
-    den = np.linalg.norm(yo)
-    frob = np.linalg.norm(yg - yo) / den if den > 0 else np.linalg.norm(yg)
-    assert frob <= OUT_FROB_MAX, f"rel Frobenius {frob:.2e}"
     ybits = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.mean(ybits == own["out_bits"]) >= own_min, "output is not the GEMM of the GPU's codes"
+    yg = O.bf16_bits_to_f32(ybits).astype(np.float64)
+    frob = _rel_frob(yg, O.bf16_bits_to_f32(ref["out_bits"]).astype(np.float64))
+    if frob > OUT_FROB_MAX:
+        # Only the effect of codes that sit at rounding near-ties (each checked above) may
+        # exceed the bar: a near-tie code may take either neighbour.  In a small output a single
+        # one can move the result by more than 1e-2.  The output must then be within the bar of
+        # the oracle's GEMM of the same codes.
+        diffs = _code_diffs(fmt, xq, wq, ref, *((xbs, wbs) if fmt == "mxfp4" else ()))
+        own_y = O.bf16_bits_to_f32(own["out_bits"]).astype(np.float64)
+        assert diffs > 0 and _rel_frob(yg, own_y) <= OUT_FROB_MAX, \
+            f"rel Frobenius {frob:.2e} with {diffs} codes at near-ties"
+
+
+def _rel_frob(a, ref):
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(a - ref) / den if den > 0 else np.linalg.norm(a)
+
+
+def _code_diffs(fmt, xq, wq, ref, xbs=None, wbs=None):
+    """Codes (and MXFP4 block scales) that differ from the oracle's."""
+    if fmt == "int8":
+        gx, gw = xq.cpu().numpy(), wq.cpu().numpy()
+    else:
+        gx, gw = O.unpack_int4(xq.cpu().numpy()), O.unpack_int4(wq.cpu().numpy())
+    if fmt == "mxfp4":  # compare E2M1 values: +0 and -0 are the same number
+        nb = ref["x"]["scales"].shape[1]
+        return int(np.count_nonzero(O.e2m1_decode(gx & 0xF) != O.e2m1_decode(ref["x"]["codes"])) +
+                   np.count_nonzero(O.e2m1_decode(gw & 0xF) != O.e2m1_decode(ref["w"]["codes"])) +
+                   np.count_nonzero(xbs.cpu().numpy()[:, :nb] != ref["x"]["scales"]) +
+                   np.count_nonzero(wbs.cpu().numpy()[:, :nb] != ref["w"]["scales"]))
+    return int(np.count_nonzero(gx != ref["x"]["codes"]) + np.count_nonzero(gw != ref["w"]["codes"]))
