@@ -13,10 +13,10 @@ from ._lib import (  # noqa: F401
     convrot_rotate_quant_act_mxfp4, convrot_quant_weight_mxfp4, convrot_mxfp4_gemm,
     convrot_mxfp4_workspace_bytes, convrot_mxfp4_linear, mx_scale_stride,
 )
-from .linear import ConvLinear4bit  # noqa: F401
+from .linear import ConvLinear4bit, ConvLinear8bit, ConvLinearFP4  # noqa: F401
 
 __all__ = [
-    "ConvLinear4bit", "ConvRotError", "load_library", "convrot_status_string", "convrot_version",
+    "ConvLinear4bit", "ConvLinear8bit", "ConvLinearFP4", "ConvRotError", "load_library", "convrot_status_string", "convrot_version",
     "convrot_padded_k", "convrot_is_power_of_4", "convrot_make_rht", "convrot_rotate_quant_act",
     "convrot_quant_weight", "convrot_w4a4_gemm", "convrot_w4a4_workspace_bytes",
     "convrot_w4a4_linear", "convrot_rotate_quant_act_i8", "convrot_quant_weight_i8",

@@ -1,8 +1,13 @@
-"""ConvLinear4bit: plug-and-play W4A4 replacement for a linear layer.
+"""ConvLinear4bit: plug-and-play W4A4 replacement for a linear layer, and its W8A8 and MXFP4
+siblings.
 
 ConvRot paper (arXiv 2512.03673), Abstract and Fig. 3: the module integrates rotation,
 quantization, GEMM and dequantization.  Weights are rotated and quantized once, offline
-(per output channel); activations are rotated and quantized per token on every call.
+(per output channel); activations are rotated and quantized per token on every call.  The
+other two code formats keep the same rotation: int8 codes with scale absmax / 127 (the HSWQ
+release notes' "Hadamard Orthogonal Rotation" form), and MXFP4 (E2M1 codes with one E8M0
+scale per 32 values; the ConvRot author notes that the rotation suits floating-point
+quantization too).
 """
 from __future__ import annotations
 
@@ -13,8 +18,15 @@ import torch
 from . import _lib
 
 
-class ConvLinear4bit(torch.nn.Module):
-    """y = dequant(int4(RHT(x)) @ int4(RHT(W))^T) + bias, output bf16."""
+class _ConvLinearBase(torch.nn.Module):
+    """Shared module logic; subclasses name the code format's entry points and buffers."""
+
+    # per format: the entry points, the code dtype, codes per weight row given K', and the
+    # scale buffer's shape and dtype
+    _code_dtype = torch.uint8
+    _quant_weight = None
+    _workspace_bytes = None
+    _linear = None
 
     def __init__(self, in_features: int, out_features: int, group_size: int = 256,
                  device=None):
@@ -24,20 +36,29 @@ class ConvLinear4bit(torch.nn.Module):
         self.group_size = int(group_size)
         self.padded_in = _lib.convrot_padded_k(self.in_features, self.group_size)
         self.register_buffer("weight_packed", torch.zeros(
-            (self.out_features, self.padded_in // 2), dtype=torch.uint8, device=device))
-        self.register_buffer("weight_scale", torch.zeros(
-            (self.out_features,), dtype=torch.float32, device=device))
+            (self.out_features, self._code_bytes(self.padded_in)), dtype=self._code_dtype,
+            device=device))
+        shape, dtype = self._scale_layout(self.out_features, self.padded_in)
+        self.register_buffer("weight_scale", torch.zeros(shape, dtype=dtype, device=device))
         self.bias: Optional[torch.Tensor] = None
         self._workspace: Optional[torch.Tensor] = None
 
+    @staticmethod
+    def _code_bytes(kp: int) -> int:
+        return kp // 2
+
+    @staticmethod
+    def _scale_layout(n: int, kp: int):
+        return (n,), torch.float32
+
     @classmethod
     def from_linear(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
-                    group_size: int = 256) -> "ConvLinear4bit":
+                    group_size: int = 256):
         """Builds the layer from a dense weight [N, K] (bf16 or fp32, on the GPU)."""
         n, k = weight.shape
         mod = cls(k, n, group_size, device=weight.device)
-        _lib.convrot_quant_weight(weight.contiguous(), group_size, mod.weight_packed,
-                                  mod.weight_scale)
+        type(mod)._quant_weight(weight.contiguous(), group_size, mod.weight_packed,
+                                mod.weight_scale)
         if bias is not None:
             mod.bias = bias.detach().to(torch.bfloat16).contiguous()
         return mod
@@ -45,10 +66,44 @@ class ConvLinear4bit(torch.nn.Module):
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
         x2 = x.reshape(-1, self.in_features).contiguous()
-        need = _lib.convrot_w4a4_workspace_bytes(x2.shape[0], self.in_features, self.group_size)
+        need = type(self)._workspace_bytes(x2.shape[0], self.in_features, self.group_size)
         if self._workspace is None or self._workspace.numel() < need or \
                 self._workspace.device != x2.device:
             self._workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
-        y = _lib.convrot_w4a4_linear(x2, self.group_size, self.weight_packed, self.weight_scale,
-                                     self.bias, workspace=self._workspace)
+        y = type(self)._linear(x2, self.group_size, self.weight_packed, self.weight_scale,
+                               self.bias, workspace=self._workspace)
         return y.reshape(*lead, self.out_features)
+
+
+class ConvLinear4bit(_ConvLinearBase):
+    """y = dequant(int4(RHT(x)) @ int4(RHT(W))^T) + bias, output bf16."""
+
+    _quant_weight = staticmethod(_lib.convrot_quant_weight)
+    _workspace_bytes = staticmethod(_lib.convrot_w4a4_workspace_bytes)
+    _linear = staticmethod(_lib.convrot_w4a4_linear)
+
+
+class ConvLinear8bit(_ConvLinearBase):
+    """The W8A8 form: int8 codes, per-token / per-channel scale absmax / 127, output bf16."""
+
+    _code_dtype = torch.int8
+    _quant_weight = staticmethod(_lib.convrot_quant_weight_i8)
+    _workspace_bytes = staticmethod(_lib.convrot_w8a8_workspace_bytes)
+    _linear = staticmethod(_lib.convrot_w8a8_linear)
+
+    @staticmethod
+    def _code_bytes(kp: int) -> int:
+        return kp
+
+
+class ConvLinearFP4(_ConvLinearBase):
+    """The MXFP4 form: E2M1 codes with E8M0 block scales on both operands, output bf16.
+    group_size must be 64, 256 or 1024."""
+
+    _quant_weight = staticmethod(_lib.convrot_quant_weight_mxfp4)
+    _workspace_bytes = staticmethod(_lib.convrot_mxfp4_workspace_bytes)
+    _linear = staticmethod(_lib.convrot_mxfp4_linear)
+
+    @staticmethod
+    def _scale_layout(n: int, kp: int):
+        return (n, _lib.mx_scale_stride(kp)), torch.uint8

@@ -223,3 +223,20 @@ def test_int8_entry_points_validate(lib):
     assert ln(wsp=A16 * 16 + 16) == E.CONVROT_ERR_ALIGN
     assert ln(nbytes=cr.convrot_w8a8_workspace_bytes(4, 64, 16) - 1) == E.CONVROT_ERR_WORKSPACE
     assert ln(M=0, wsp=None) == E.CONVROT_OK
+
+
+def test_modules_allocate_each_formats_buffers(lib):
+    """Host-side shapes and dtypes of the three linear modules' weight buffers (CPU tensors)."""
+    K, N, g = 3100, 200, 256
+    kp = O.padded_k(K, g)
+    m4 = cr.ConvLinear4bit(K, N, g)
+    assert tuple(m4.weight_packed.shape) == (N, kp // 2)
+    assert str(m4.weight_packed.dtype) == "torch.uint8"
+    assert tuple(m4.weight_scale.shape) == (N,) and str(m4.weight_scale.dtype) == "torch.float32"
+    m8 = cr.ConvLinear8bit(K, N, g)
+    assert tuple(m8.weight_packed.shape) == (N, kp) and str(m8.weight_packed.dtype) == "torch.int8"
+    assert tuple(m8.weight_scale.shape) == (N,)
+    mf = cr.ConvLinearFP4(K, N, g)
+    assert tuple(mf.weight_packed.shape) == (N, kp // 2)
+    assert tuple(mf.weight_scale.shape) == (N, 4 * (-(-kp // 128)))
+    assert str(mf.weight_scale.dtype) == "torch.uint8"

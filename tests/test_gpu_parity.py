@@ -271,6 +271,34 @@ def test_convlinear4bit_module(cr):
     assert frob <= OUT_FROB_MAX
 
 
+@pytest.mark.parametrize("codes", ["int4", "int8", "mxfp4"])
+def test_linear_modules_match_functional_api(cr, codes):
+    """Each format's module: a 3-D input, bias; output bit-identical to the functional call on
+    the same weights, and within the end-to-end bar of the oracle."""
+    _announce(f"linear module {codes}")
+    wl = wk.custom("m", 96, 700, 160, 256, bias_std=0.01)
+    x, w, b = wk.activations(wl), wk.weights(wl), wk.bias(wl)
+    cls, quant, linear, oracle = {
+        "int4": (cr.ConvLinear4bit, cr.convrot_quant_weight, cr.convrot_w4a4_linear,
+                 O.convlinear4bit),
+        "int8": (cr.ConvLinear8bit, cr.convrot_quant_weight_i8, cr.convrot_w8a8_linear,
+                 O.convlinear8bit),
+        "mxfp4": (cr.ConvLinearFP4, cr.convrot_quant_weight_mxfp4, cr.convrot_mxfp4_linear,
+                  O.convlinear_fp4),
+    }[codes]
+    wd, bd, xd = _to_dev(w, "bf16"), _to_dev(b, "bf16").to(torch.bfloat16), _to_dev(x, "bf16")
+    layer = cls.from_linear(wd, bd, group_size=256)
+    y = layer(xd.reshape(2, 48, 700))
+    assert y.shape == (2, 48, 160) and y.dtype == torch.bfloat16
+    wq, ws = quant(wd, 256)
+    y_f = linear(xd, 256, wq, ws, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(y.reshape(96, 160).view(torch.int16), y_f.view(torch.int16))
+    yo = O.bf16_bits_to_f32(oracle(x, w, b, 256)["out_bits"]).astype(np.float64)
+    frob = np.linalg.norm(y.reshape(96, 160).float().cpu().numpy() - yo) / np.linalg.norm(yo)
+    assert frob <= OUT_FROB_MAX
+
+
 # Full-size workloads in the launch configuration the benchmark times; the oracle checks a
 # sample of rows (rows are independent) including every outlier row it picks.
 FULL = ["rotate_quant", "attn_proj", "mlp_down", "proj_out", "proj_out_padded", "few_tokens"]
