@@ -46,9 +46,10 @@ Readings taken where the pages are silent:
   * dequant order: z = fp32(fp32(fp32(acc) * sx[m]) * sw[n]); z = fp32(z + b);
     output = bf16 round-to-nearest-even of z.
 
-Every function is pinned in ``tests/test_oracle_pins.py`` against closed
-forms, invariants, brute force or library routines; ``reference_linear_fp64``
-is report-only (parity unpinned: the pages print no per-layer error).
+Every function is pinned in ``tests/oracle_pins.py`` (run by
+``tests/test_oracle_pins.py``) against closed forms, invariants, brute force,
+exact rational arithmetic or library routines; ``tests/test_oracle_mutations.py``
+plants plausible mistakes in copies of it and checks that a pin fails.
 """
 from __future__ import annotations
 
@@ -382,11 +383,3 @@ def convlinear_fp4(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], g: 
     wr = quantize_weight_mxfp4(w, g)
     lin = mxfp4_linear_from_codes(xr["codes"], xr["scales"], wr["codes"], wr["scales"], bias)
     return {"x": xr, "w": wr, **lin}
-
-
-def reference_linear_fp64(x, w, bias=None) -> np.ndarray:
-    """Unquantized X W^T + b in float64 (report-only error reference; parity unpinned)."""
-    y = np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
-    if bias is not None:
-        y = y + np.asarray(bias, dtype=np.float64)[None, :]
-    return y

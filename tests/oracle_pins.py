@@ -262,6 +262,58 @@ def pin_rotation_exact_fsum(o):
             assert y[m, p] == math.fsum(terms) / 2 ** k
 
 
+def _rne_f32_exact(v: float) -> float:
+    """Round-to-nearest-even of a finite float64 to the float32 grid, in exact rational
+    arithmetic: the quantum is 2^(e - 23) in the binade [2^e, 2^(e + 1)), and 2^-149 below
+    2^-126 (the subnormals)."""
+    from fractions import Fraction
+    if v == 0.0:
+        return v
+    a = Fraction(abs(v))
+    e = math.frexp(abs(v))[1] - 1          # 2^e <= |v| < 2^(e + 1)
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    lo = n.numerator // n.denominator
+    rem = n - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    return math.copysign(float(lo * quantum), v)
+
+
+def pin_to_f32(o):
+    """The single fp64 -> fp32 rounding of the rotated values (it fixes every scale and code):
+    round to nearest, ties to the even significand, also among the subnormals.  Checked
+    against exact rational rounding and against C's float conversion (struct 'f'), on random
+    values of every magnitude and on values constructed exactly halfway between adjacent
+    float32 numbers (and one float64 step to either side of the midpoint)."""
+    import struct
+    rng = np.random.default_rng(40)
+    mags = np.concatenate([rng.uniform(-126, 127, 3000), rng.uniform(-149, -126, 1000)])
+    vals = np.exp2(mags) * rng.uniform(1.0, 2.0, mags.size)
+    vals *= np.where(rng.random(vals.size) < 0.5, -1.0, 1.0)
+    got = o.to_f32(vals)
+    assert got.dtype == np.float32
+    for v, r in zip(vals.tolist(), got.tolist()):
+        want = _rne_f32_exact(v)
+        assert r == want, (v, r, want)
+        assert struct.unpack("<f", struct.pack("<f", v))[0] == want
+    # midpoints between float32 neighbours b and b + 1: normal, subnormal, binade edges
+    bits = np.concatenate([rng.integers(0x00800000, 0x7F7FFFFE, 3000),
+                           rng.integers(0, 0x007FFFFF, 1000),
+                           [0, 1, 2, 0x007FFFFE, 0x007FFFFF, 0x00800000, 0x3F7FFFFF,
+                            0x3F800000, 0x7F7FFFFD]]).astype(np.uint32)
+    lo = bits.view(np.float32).astype(np.float64)
+    hi = (bits + np.uint32(1)).view(np.float32).astype(np.float64)
+    mid = (lo + hi) / 2.0                   # exact: both have 24-bit significands
+    even = np.where(bits % 2 == 0, lo, hi)
+    below, above = np.nextafter(mid, -np.inf), np.nextafter(mid, np.inf)
+    for sign in (1.0, -1.0):
+        assert np.array_equal(o.to_f32(sign * mid).astype(np.float64), sign * even)
+        assert np.array_equal(o.to_f32(sign * below).astype(np.float64), sign * lo)
+        assert np.array_equal(o.to_f32(sign * above).astype(np.float64), sign * hi)
+    assert np.signbit(o.to_f32(np.array([-0.0, -2.0 ** -151]))).all()   # -0 stays -0
+
+
 # ---------------------------------------------------------------- quantization
 def pin_quant_round_trip(o):
     """Rows s * (integers in [-7, 7]) with 7 present come back exactly."""

@@ -124,6 +124,21 @@ def _e2m1_no_negative_zero(t):
     return np.where(c == 8, 0, c).astype(np.uint8)
 
 
+def _to_f32_truncate(y):
+    # drops the 29 low significand bits: rounds toward zero instead of to nearest even
+    b = np.asarray(y, dtype=np.float64).view(np.uint64) & ~np.uint64((1 << 29) - 1)
+    return b.view(np.float64).astype(np.float32)
+
+
+def _to_f32_ties_away(y):
+    # nearest, but exact midpoints go to the neighbour away from zero
+    y = np.asarray(y, dtype=np.float64)
+    r = y.astype(np.float32)
+    away = np.nextafter(r, np.copysign(np.float32(np.inf), r))
+    mid = (r.astype(np.float64) + away.astype(np.float64)) / 2.0
+    return np.where(mid == y, away, r).astype(np.float32)
+
+
 def _mx_values_unscaled(codes, e8m0):
     # decoded codes without their block scale
     return O.e2m1_decode(codes)
@@ -156,6 +171,8 @@ MUTATIONS = {
     "mx_emax_3": ({"E2M1_EMAX": 3}, ["pin_mx_block_scale", "pin_mxfp4_round_trip",
                                      "pin_mxfp4_end_to_end_closed_form"]),
     "mx_block_16": ({"MX_BLOCK": 16}, ["pin_mx_block_scale"]),
+    "to_f32_truncation": ({"to_f32": _to_f32_truncate}, ["pin_to_f32"]),
+    "to_f32_ties_away": ({"to_f32": _to_f32_ties_away}, ["pin_to_f32"]),
     "mx_values_unscaled": ({"mxfp4_values": _mx_values_unscaled},
                            ["pin_mxfp4_gemm_brute_force", "pin_mxfp4_round_trip"]),
 }
