@@ -123,6 +123,69 @@ def _require_device(*ts: Optional[torch.Tensor]) -> torch.device:
     return dev
 
 
+_CODE_BYTES = (torch.uint8, torch.int8)   # code tensors: one byte per element, either signedness
+
+
+def _is_tensor(t, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+
+
+def _mat(t: Optional[torch.Tensor], name: str, rows: int, cols: int, dtypes) -> None:
+    """A caller-supplied 2-D buffer: contiguous, shape (rows, cols), one of dtypes (None passes:
+    the binding allocates it)."""
+    if t is None:
+        return
+    _is_tensor(t, name)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} must have shape ({rows}, {cols}), got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _vec(t: Optional[torch.Tensor], name: str, n: int, dtype: torch.dtype) -> None:
+    """A per-row or per-column vector: contiguous, n elements as (n,) or (n, 1), dtype."""
+    if t is None:
+        return
+    _is_tensor(t, name)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) not in ((n,), (n, 1)):
+        raise ValueError(f"{name} must have {n} elements as ({n},) or ({n}, 1), got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _codes_2d(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    _is_tensor(t, name)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got {t.dim()} dimensions")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def _activations(x: torch.Tensor, contiguous: bool, name: str = "x") -> Tuple[int, int]:
+    """x [M, K], bf16 or fp32; rows may be strided unless the entry point needs row stride K."""
+    _is_tensor(x, name)
+    if x.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got {x.dim()} dimensions")
+    if contiguous and not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous 2-D tensor")
+    if x.stride(1) != 1 and x.shape[1] > 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    _dtype_code(x)
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def _workspace(ws: torch.Tensor) -> int:
+    """Bytes of a caller-supplied workspace (contiguous; any dtype)."""
+    _is_tensor(ws, "workspace")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 # ----------------------------------------------------------------- host helpers
 def convrot_status_string(status: int) -> str:
     return load_library().convrot_status_string(int(status)).decode()
@@ -157,87 +220,161 @@ def convrot_w4a4_workspace_bytes(M: int, K: int, g: int) -> int:
 
 
 # ----------------------------------------------------------------- device entry points
+# Every entry point checks each tensor argument on the host first (device, dtype, contiguity
+# and the exact shape implied by M, N and K'), so that no kernel reads or writes past a buffer.
+def _rotate(fn, x, g, xq, xs, xrot, want_rotated, code_cols, code_dtype, scale_shape,
+            scale_dtype):
+    M, K = _activations(x, contiguous=False)
+    Kp = convrot_padded_k(K, g)
+    cols = code_cols(Kp)
+    _mat(xq, "xq", M, cols, _CODE_BYTES)
+    sshape = scale_shape(M, Kp)
+    if len(sshape) == 1:
+        _vec(xs, "xs", M, scale_dtype)
+    else:
+        _mat(xs, "scales", sshape[0], sshape[1], (scale_dtype,))
+    _mat(xrot, "xrot", M, Kp, (torch.float32,))
+    dev = _require_device(x, xq, xs, xrot)
+    if xq is None:
+        xq = torch.empty((M, cols), dtype=code_dtype, device=dev)
+    if xs is None:
+        xs = torch.empty(sshape, dtype=scale_dtype, device=dev)
+    if xrot is None and want_rotated:
+        xrot = torch.empty((M, Kp), dtype=torch.float32, device=dev)
+    st = fn(_ptr(x), _dtype_code(x), M, K, x.stride(0), g, _ptr(xq), _ptr(xs), _ptr(xrot),
+            _stream(dev))
+    _check(st, g)
+    return (xq, xs, xrot) if xrot is not None else (xq, xs)
+
+
+def _quant_weight(fn, w, g, wq, ws, code_cols, code_dtype, scale_shape, scale_dtype):
+    N, K = _activations(w, contiguous=True, name="w")
+    Kp = convrot_padded_k(K, g)
+    cols = code_cols(Kp)
+    _mat(wq, "wq", N, cols, _CODE_BYTES)
+    sshape = scale_shape(N, Kp)
+    if len(sshape) == 1:
+        _vec(ws, "ws", N, scale_dtype)
+    else:
+        _mat(ws, "scales", sshape[0], sshape[1], (scale_dtype,))
+    dev = _require_device(w, wq, ws)
+    if wq is None:
+        wq = torch.empty((N, cols), dtype=code_dtype, device=dev)
+    if ws is None:
+        ws = torch.empty(sshape, dtype=scale_dtype, device=dev)
+    st = fn(_ptr(w), _dtype_code(w), N, K, g, _ptr(wq), _ptr(ws), _stream(dev))
+    _check(st, g)
+    return wq, ws
+
+
+def _row_scale_shape(rows: int, kp: int):
+    return (rows,)
+
+
+def _mx_scale_shape(rows: int, kp: int):
+    return (rows, mx_scale_stride(kp))
+
+
+def _half(kp: int) -> int:
+    return kp // 2
+
+
+def _full(kp: int) -> int:
+    return kp
+
+
+def _gemm_checks(xq, xs, wq, ws, bias, y, cols_per_kp, mx: bool):
+    """Shapes of a GEMM call from its code operands; returns (M, N, K')."""
+    M, cols = _codes_2d(xq, "xq")
+    N, wcols = _codes_2d(wq, "wq")
+    if wcols != cols:
+        raise ValueError(f"xq and wq must have the same depth, got {cols} and {wcols} bytes")
+    Kp = cols * cols_per_kp
+    _mat(xq, "xq", M, cols, _CODE_BYTES)
+    _mat(wq, "wq", N, cols, _CODE_BYTES)
+    if mx:
+        _mat(xs, "xbs", M, mx_scale_stride(Kp), (torch.uint8,))
+        _mat(ws, "wbs", N, mx_scale_stride(Kp), (torch.uint8,))
+    else:
+        _is_tensor(xs, "xs")
+        _is_tensor(ws, "ws")
+        _vec(xs, "xs", M, torch.float32)
+        _vec(ws, "ws", N, torch.float32)
+    _vec(bias, "bias", N, torch.bfloat16)
+    _mat(y, "y", M, N, (torch.bfloat16,))
+    return M, N, Kp
+
+
+def _gemm(fn, xq, xs, wq, ws, bias, y, want_acc, cols_per_kp, mx, acc_dtype):
+    M, N, Kp = _gemm_checks(xq, xs, wq, ws, bias, y, cols_per_kp, mx)
+    dev = _require_device(xq, xs, wq, ws, bias, y)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    acc = torch.empty((M, N), dtype=acc_dtype, device=dev) if want_acc else None
+    st = fn(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(bias), M, N, Kp, _ptr(y), _ptr(acc),
+            _stream(dev))
+    _check(st)
+    return (y, acc) if want_acc else y
+
+
+def _linear(fn, need_fn, x, g, wq, ws, bias, y, workspace, code_cols, mx):
+    M, K = _activations(x, contiguous=True)
+    Kp = convrot_padded_k(K, g)
+    N, cols = _codes_2d(wq, "wq")
+    if cols != code_cols(Kp):
+        raise ValueError(f"wq must have {code_cols(Kp)} bytes per row for K={K}, g={g} "
+                         f"(K' = {Kp}), got {cols}")
+    _mat(wq, "wq", N, cols, _CODE_BYTES)
+    if mx:
+        _mat(ws, "wbs", N, mx_scale_stride(Kp), (torch.uint8,))
+    else:
+        _is_tensor(ws, "ws")
+        _vec(ws, "ws", N, torch.float32)
+    _vec(bias, "bias", N, torch.bfloat16)
+    _mat(y, "y", M, N, (torch.bfloat16,))
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _require_device(x, wq, ws, bias, y, workspace)
+    if workspace is None:
+        workspace = torch.empty((max(need_fn(M, K, g), 1),), dtype=torch.uint8, device=dev)
+    nbytes = _workspace(workspace)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    st = fn(_ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(ws), N, _ptr(bias), _ptr(y),
+            _ptr(workspace), nbytes, _stream(dev))
+    _check(st, g)
+    return y
+
+
 def convrot_rotate_quant_act(x: torch.Tensor, g: int, xq: Optional[torch.Tensor] = None,
                              xs: Optional[torch.Tensor] = None, xrot: Optional[torch.Tensor] = None,
                              want_rotated: bool = False):
     """x [M, K] (bf16/fp32, row stride x.stride(0)) -> (xq uint8 [M, K'/2], xs fp32 [M][, xrot])."""
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be 2-D with unit column stride")
-    M, K = x.shape
-    Kp = convrot_padded_k(K, g)
-    dev = _require_device(x, xq, xs, xrot)
-    if xq is None:
-        xq = torch.empty((M, Kp // 2), dtype=torch.uint8, device=dev)
-    if xs is None:
-        xs = torch.empty((M,), dtype=torch.float32, device=dev)
-    if xrot is None and want_rotated:
-        xrot = torch.empty((M, Kp), dtype=torch.float32, device=dev)
-    st = load_library().convrot_rotate_quant_act(
-        _ptr(x), _dtype_code(x), M, K, x.stride(0), g, _ptr(xq), _ptr(xs), _ptr(xrot),
-        _stream(dev))
-    _check(st, g)
-    return (xq, xs, xrot) if xrot is not None else (xq, xs)
+    return _rotate(load_library().convrot_rotate_quant_act, x, g, xq, xs, xrot, want_rotated,
+                   _half, torch.uint8, _row_scale_shape, torch.float32)
 
 
 def convrot_quant_weight(w: torch.Tensor, g: int, wq: Optional[torch.Tensor] = None,
                          ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """w [N, K] contiguous (bf16/fp32) -> (wq uint8 [N, K'/2], ws fp32 [N])."""
-    if w.dim() != 2 or not w.is_contiguous():
-        raise ValueError("w must be a contiguous 2-D tensor")
-    N, K = w.shape
-    Kp = convrot_padded_k(K, g)
-    dev = _require_device(w, wq, ws)
-    if wq is None:
-        wq = torch.empty((N, Kp // 2), dtype=torch.uint8, device=dev)
-    if ws is None:
-        ws = torch.empty((N,), dtype=torch.float32, device=dev)
-    st = load_library().convrot_quant_weight(_ptr(w), _dtype_code(w), N, K, g, _ptr(wq), _ptr(ws),
-                                             _stream(dev))
-    _check(st, g)
-    return wq, ws
+    return _quant_weight(load_library().convrot_quant_weight, w, g, wq, ws, _half, torch.uint8,
+                         _row_scale_shape, torch.float32)
 
 
 def convrot_w4a4_gemm(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
                       bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                       want_acc: bool = False):
     """Packed int4 GEMM + dequant: y bf16 [M, N] (and the int32 sums [M, N] if want_acc)."""
-    M, half = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != half:
-        raise ValueError("xq and wq must have the same packed depth")
-    if bias is not None and bias.dtype != torch.bfloat16:
-        raise TypeError("bias must be bfloat16")
-    dev = _require_device(xq, xs, wq, ws, bias, y)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
-    st = load_library().convrot_w4a4_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(bias), M, N,
-                                          2 * half, _ptr(y), _ptr(acc), _stream(dev))
-    _check(st)
-    return (y, acc) if want_acc else y
+    return _gemm(load_library().convrot_w4a4_gemm, xq, xs, wq, ws, bias, y, want_acc, 2, False,
+                 torch.int32)
 
 
 def convrot_w4a4_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Tensor,
                         bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """ConvLinear4bit forward: x [M, K] contiguous -> y bf16 [M, N]."""
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
-    M, K = x.shape
-    N = wq.shape[0]
-    if bias is not None and bias.dtype != torch.bfloat16:
-        raise TypeError("bias must be bfloat16")
-    dev = _require_device(x, wq, ws, bias, y, workspace)
-    need = convrot_w4a4_workspace_bytes(M, K, g)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    st = load_library().convrot_w4a4_linear(
-        _ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(ws), N, _ptr(bias), _ptr(y),
-        _ptr(workspace), workspace.numel(), _stream(dev))
-    _check(st, g)
-    return y
+    return _linear(load_library().convrot_w4a4_linear, convrot_w4a4_workspace_bytes, x, g, wq,
+                   ws, bias, y, workspace, _half, False)
 
 
 # ----------------------------------------------------------------- INT8 (W8A8) variant
@@ -249,83 +386,31 @@ def convrot_rotate_quant_act_i8(x: torch.Tensor, g: int, xq: Optional[torch.Tens
                                 xs: Optional[torch.Tensor] = None,
                                 xrot: Optional[torch.Tensor] = None, want_rotated: bool = False):
     """x [M, K] (bf16/fp32, row stride x.stride(0)) -> (xq int8 [M, K'], xs fp32 [M][, xrot])."""
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be 2-D with unit column stride")
-    M, K = x.shape
-    Kp = convrot_padded_k(K, g)
-    dev = _require_device(x, xq, xs, xrot)
-    if xq is None:
-        xq = torch.empty((M, Kp), dtype=torch.int8, device=dev)
-    if xs is None:
-        xs = torch.empty((M,), dtype=torch.float32, device=dev)
-    if xrot is None and want_rotated:
-        xrot = torch.empty((M, Kp), dtype=torch.float32, device=dev)
-    st = load_library().convrot_rotate_quant_act_i8(
-        _ptr(x), _dtype_code(x), M, K, x.stride(0), g, _ptr(xq), _ptr(xs), _ptr(xrot),
-        _stream(dev))
-    _check(st, g)
-    return (xq, xs, xrot) if xrot is not None else (xq, xs)
+    return _rotate(load_library().convrot_rotate_quant_act_i8, x, g, xq, xs, xrot, want_rotated,
+                   _full, torch.int8, _row_scale_shape, torch.float32)
 
 
 def convrot_quant_weight_i8(w: torch.Tensor, g: int, wq: Optional[torch.Tensor] = None,
                             ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """w [N, K] contiguous (bf16/fp32) -> (wq int8 [N, K'], ws fp32 [N])."""
-    if w.dim() != 2 or not w.is_contiguous():
-        raise ValueError("w must be a contiguous 2-D tensor")
-    N, K = w.shape
-    Kp = convrot_padded_k(K, g)
-    dev = _require_device(w, wq, ws)
-    if wq is None:
-        wq = torch.empty((N, Kp), dtype=torch.int8, device=dev)
-    if ws is None:
-        ws = torch.empty((N,), dtype=torch.float32, device=dev)
-    st = load_library().convrot_quant_weight_i8(_ptr(w), _dtype_code(w), N, K, g, _ptr(wq),
-                                                _ptr(ws), _stream(dev))
-    _check(st, g)
-    return wq, ws
+    return _quant_weight(load_library().convrot_quant_weight_i8, w, g, wq, ws, _full, torch.int8,
+                         _row_scale_shape, torch.float32)
 
 
 def convrot_w8a8_gemm(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
                       bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                       want_acc: bool = False):
     """int8 GEMM + dequant: y bf16 [M, N] (and the int32 sums [M, N] if want_acc)."""
-    M, Kp = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != Kp:
-        raise ValueError("xq and wq must have the same depth")
-    if bias is not None and bias.dtype != torch.bfloat16:
-        raise TypeError("bias must be bfloat16")
-    dev = _require_device(xq, xs, wq, ws, bias, y)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    acc = torch.empty((M, N), dtype=torch.int32, device=dev) if want_acc else None
-    st = load_library().convrot_w8a8_gemm(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(bias), M, N,
-                                          Kp, _ptr(y), _ptr(acc), _stream(dev))
-    _check(st)
-    return (y, acc) if want_acc else y
+    return _gemm(load_library().convrot_w8a8_gemm, xq, xs, wq, ws, bias, y, want_acc, 1, False,
+                 torch.int32)
 
 
 def convrot_w8a8_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Tensor,
                         bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """W8A8 ConvRot forward: x [M, K] contiguous -> y bf16 [M, N]."""
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
-    M, K = x.shape
-    N = wq.shape[0]
-    if bias is not None and bias.dtype != torch.bfloat16:
-        raise TypeError("bias must be bfloat16")
-    dev = _require_device(x, wq, ws, bias, y, workspace)
-    need = convrot_w8a8_workspace_bytes(M, K, g)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    st = load_library().convrot_w8a8_linear(
-        _ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(ws), N, _ptr(bias), _ptr(y),
-        _ptr(workspace), workspace.numel(), _stream(dev))
-    _check(st, g)
-    return y
+    return _linear(load_library().convrot_w8a8_linear, convrot_w8a8_workspace_bytes, x, g, wq,
+                   ws, bias, y, workspace, _full, False)
 
 
 def mx_scale_stride(kp: int) -> int:
@@ -339,63 +424,23 @@ def convrot_rotate_quant_act_mxfp4(x: torch.Tensor, g: int, xq: Optional[torch.T
     """x [M, K] (bf16/fp32, row stride x.stride(0)) -> (xq uint8 [M, K'/2] E2M1 codes,
     xbs uint8 [M, S] E8M0 block scales (S = 4 ceil(K'/128): K'/32 blocks, zero padding)
     [, xrot fp32 [M, K']])."""
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be 2-D with unit column stride")
-    M, K = x.shape
-    Kp = convrot_padded_k(K, g)
-    dev = _require_device(x, xq, xbs, xrot)
-    if xq is None:
-        xq = torch.empty((M, Kp // 2), dtype=torch.uint8, device=dev)
-    if xbs is None:
-        xbs = torch.empty((M, mx_scale_stride(Kp)), dtype=torch.uint8, device=dev)
-    if xrot is None and want_rotated:
-        xrot = torch.empty((M, Kp), dtype=torch.float32, device=dev)
-    st = load_library().convrot_rotate_quant_act_mxfp4(
-        _ptr(x), _dtype_code(x), M, K, x.stride(0), g, _ptr(xq), _ptr(xbs), _ptr(xrot),
-        _stream(dev))
-    _check(st, g)
-    return (xq, xbs, xrot) if xrot is not None else (xq, xbs)
+    return _rotate(load_library().convrot_rotate_quant_act_mxfp4, x, g, xq, xbs, xrot,
+                   want_rotated, _half, torch.uint8, _mx_scale_shape, torch.uint8)
 
 
 def convrot_quant_weight_mxfp4(w: torch.Tensor, g: int, wq: Optional[torch.Tensor] = None,
                                wbs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """w [N, K] contiguous (bf16/fp32) -> (wq uint8 [N, K'/2], wbs uint8 [N, S])."""
-    if w.dim() != 2 or not w.is_contiguous():
-        raise ValueError("w must be a contiguous 2-D tensor")
-    N, K = w.shape
-    Kp = convrot_padded_k(K, g)
-    dev = _require_device(w, wq, wbs)
-    if wq is None:
-        wq = torch.empty((N, Kp // 2), dtype=torch.uint8, device=dev)
-    if wbs is None:
-        wbs = torch.empty((N, mx_scale_stride(Kp)), dtype=torch.uint8, device=dev)
-    st = load_library().convrot_quant_weight_mxfp4(_ptr(w), _dtype_code(w), N, K, g, _ptr(wq),
-                                                   _ptr(wbs), _stream(dev))
-    _check(st, g)
-    return wq, wbs
+    return _quant_weight(load_library().convrot_quant_weight_mxfp4, w, g, wq, wbs, _half,
+                         torch.uint8, _mx_scale_shape, torch.uint8)
 
 
 def convrot_mxfp4_gemm(xq: torch.Tensor, xbs: torch.Tensor, wq: torch.Tensor, wbs: torch.Tensor,
                        bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                        want_acc: bool = False):
     """MXFP4 GEMM: y bf16 [M, N] (and the fp32 sums [M, N] before the bias if want_acc)."""
-    M, half = xq.shape
-    N = wq.shape[0]
-    Kp = 2 * half
-    if wq.shape[1] != half:
-        raise ValueError("xq and wq must have the same depth")
-    if xbs.shape != (M, mx_scale_stride(Kp)) or wbs.shape != (N, mx_scale_stride(Kp)):
-        raise ValueError("block scales must be [rows, 4 ceil(K'/128)]")
-    if bias is not None and bias.dtype != torch.bfloat16:
-        raise TypeError("bias must be bfloat16")
-    dev = _require_device(xq, xbs, wq, wbs, bias, y)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    acc = torch.empty((M, N), dtype=torch.float32, device=dev) if want_acc else None
-    st = load_library().convrot_mxfp4_gemm(_ptr(xq), _ptr(xbs), _ptr(wq), _ptr(wbs), _ptr(bias), M,
-                                           N, Kp, _ptr(y), _ptr(acc), _stream(dev))
-    _check(st)
-    return (y, acc) if want_acc else y
+    return _gemm(load_library().convrot_mxfp4_gemm, xq, xbs, wq, wbs, bias, y, want_acc, 2, True,
+                 torch.float32)
 
 
 def convrot_mxfp4_workspace_bytes(M: int, K: int, g: int) -> int:
@@ -406,18 +451,5 @@ def convrot_mxfp4_linear(x: torch.Tensor, g: int, wq: torch.Tensor, wbs: torch.T
                          bias: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The MXFP4 ConvRot forward pass: x [M, K] contiguous -> y bf16 [M, N]."""
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous 2-D tensor")
-    M, K = x.shape
-    N = wq.shape[0]
-    dev = _require_device(x, wq, wbs, bias, y, workspace)
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    need = convrot_mxfp4_workspace_bytes(M, K, g)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    st = load_library().convrot_mxfp4_linear(_ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(wbs),
-                                             N, _ptr(bias), _ptr(y), _ptr(workspace),
-                                             workspace.numel(), _stream(dev))
-    _check(st, g)
-    return y
+    return _linear(load_library().convrot_mxfp4_linear, convrot_mxfp4_workspace_bytes, x, g, wq,
+                   wbs, bias, y, workspace, _half, True)

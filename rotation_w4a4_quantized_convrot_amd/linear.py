@@ -29,7 +29,7 @@ class _ConvLinearBase(torch.nn.Module):
     _linear = None
 
     def __init__(self, in_features: int, out_features: int, group_size: int = 256,
-                 device=None):
+                 bias: bool = False, device=None):
         super().__init__()
         self.in_features = int(in_features)
         self.out_features = int(out_features)
@@ -40,8 +40,9 @@ class _ConvLinearBase(torch.nn.Module):
             device=device))
         shape, dtype = self._scale_layout(self.out_features, self.padded_in)
         self.register_buffer("weight_scale", torch.zeros(shape, dtype=dtype, device=device))
-        self.bias: Optional[torch.Tensor] = None
-        self._workspace: Optional[torch.Tensor] = None
+        # bf16 [N], or None; a buffer, so that state_dict() and .to() carry it with the weights
+        self.register_buffer("bias", torch.zeros((self.out_features,), dtype=torch.bfloat16,
+                                                 device=device) if bias else None)
 
     @staticmethod
     def _code_bytes(kp: int) -> int:
@@ -54,25 +55,27 @@ class _ConvLinearBase(torch.nn.Module):
     @classmethod
     def from_linear(cls, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
                     group_size: int = 256):
-        """Builds the layer from a dense weight [N, K] (bf16 or fp32, on the GPU)."""
+        """Builds the layer from a dense weight [N, K] (bf16 or fp32, on the GPU) and an
+        optional bias of N elements."""
+        if weight.dim() != 2:
+            raise ValueError(f"weight must be 2-D [N, K], got shape {tuple(weight.shape)}")
         n, k = weight.shape
-        mod = cls(k, n, group_size, device=weight.device)
+        if bias is not None and bias.numel() != n:
+            raise ValueError(f"bias must have {n} elements (one per output), got {bias.numel()}")
+        mod = cls(k, n, group_size, bias=bias is not None, device=weight.device)
         type(mod)._quant_weight(weight.contiguous(), group_size, mod.weight_packed,
                                 mod.weight_scale)
         if bias is not None:
-            mod.bias = bias.detach().to(torch.bfloat16).contiguous()
+            mod.bias.copy_(bias.detach().reshape(n).to(torch.bfloat16))
         return mod
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
         x2 = x.reshape(-1, self.in_features).contiguous()
-        need = type(self)._workspace_bytes(x2.shape[0], self.in_features, self.group_size)
-        if self._workspace is None or self._workspace.numel() < need or \
-                self._workspace.device != x2.device:
-            self._workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
-        y = type(self)._linear(x2, self.group_size, self.weight_packed, self.weight_scale,
-                               self.bias, workspace=self._workspace)
-        return y.reshape(*lead, self.out_features)
+        # The activation codes live in a workspace from the caching allocator, per call: it is
+        # stream-ordered, so forward passes on different streams never share one.
+        return type(self)._linear(x2, self.group_size, self.weight_packed, self.weight_scale,
+                                  self.bias).reshape(*lead, self.out_features)
 
 
 class ConvLinear4bit(_ConvLinearBase):
