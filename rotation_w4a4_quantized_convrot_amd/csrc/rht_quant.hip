@@ -554,13 +554,31 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
 
     // Codes use the fp32 maximum; they agree with the exact one except at rounding ties.
     mrow = slot_used ? __uint_as_float(rmax[rloc < R ? rloc : 0]) : 0.0f;
-    const float inv = mrow > 0.0f ? kQmax / mrow : 0.0f;
+    // A row whose scale max / q_max falls below 2^-126 (a subnormal scale) would see the
+    // reciprocal q_max / max overflow or lose precision: such rows (rare; the wave branches
+    // only when it holds one) divide each value by the row's fp32 scale instead, as the
+    // definition does, clamp to the code range (a subnormal scale can round down far enough
+    // for a quotient to pass q_max + 1/2) and round with the same magic-number add.  A scale
+    // that underflows to zero gives zero codes, as for an all-zero row.
+    const bool tiny = mrow > 0.0f && mrow < kQmax * 0x1p-126f;
+    const bool any_tiny = __ballot(tiny) != 0;
+    const float inv = mrow > 0.0f && !tiny ? kQmax / mrow : 0.0f;
+    const float tiny_scale = tiny ? __fdiv_rn(mrow, kQmax) : 0.0f;
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       uint32_t bits[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         bits[e] = __float_as_uint(__builtin_fmaf(v[8 * r + e], inv, kMagic));
+      if (any_tiny && tiny) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          bits[e] = __float_as_uint(__fadd_rn(
+              tiny_scale > 0.0f
+                  ? fminf(fmaxf(__fdiv_rn(v[8 * r + e], tiny_scale), -kQmax - 1.0f), kQmax)
+                  : 0.0f,
+              kMagic));
+      }
       if constexpr (QB == 4) {
         const uint32_t lo = lshl_or<12>(bits[3], lshl_or<8>(bits[2], lshl_or<4>(bits[1], bits[0])));
         const uint32_t hi = lshl_or<12>(bits[7], lshl_or<8>(bits[6], lshl_or<4>(bits[5], bits[4])));
