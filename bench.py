@@ -11,8 +11,9 @@ Prints ONE JSON line.  `value` is the full-layer throughput 2 M N K' / step time
 timed steps.  The `roofline` object is for the dominant kernel (the GEMM, int8 matrix
 cores); the rotate+quantize kernel's HBM roofline is reported alongside.  Each kernel's
 launch duration comes from HIP events on the launch stream around batches of back-to-back
-launches of that kernel.  The CPU oracle is timed over whole passes of the same layer
-(`cpu_baseline`).
+launches of that kernel, after a time-based ramp of launches that brings the clocks to their
+sustained level; this runs before the warm-up and timed steps.  The CPU oracle is timed over
+whole passes of the same layer (`cpu_baseline`).
 
 `--codes int8` measures the W8A8 variant the same way (convrot_rotate_quant_act_i8 and
 convrot_w8a8_gemm, the kernels convrot_w8a8_linear enqueues) and prints its own line;
@@ -49,6 +50,11 @@ def parse():
     p.add_argument("--codes", choices=("int4", "int8", "mxfp4"), default="int4",
                    help="int4: the W4A4 layer (default); int8: the W8A8 variant; mxfp4: the "
                         "floating-point 4-bit variant")
+    p.add_argument("--ramp-seconds", type=float, default=0.2,
+                   help="back-to-back launches of each kernel before its timed batches")
+    p.add_argument("--batches", type=int, default=5)
+    p.add_argument("--batch-launches", type=int, default=200,
+                   help="launches per timed batch of each kernel")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = all)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -141,15 +147,45 @@ def gpu_bench(args, wl):
                    stream)
         return st
 
+    hip = Hip()
+    e0, e1 = hip.event(), hip.event()
+
+    # Launch duration of each kernel: the kernel alone, launched back to back on the launch
+    # stream (the activations still rotate through the HBM-sized buffer set), first for
+    # --ramp-seconds of wall time so that the clocks reach the level they hold under
+    # sustained load (a GPU coming out of idle runs the first milliseconds slower), then
+    # --batches batches of --batch-launches launches with events around each batch.  This
+    # does not depend on --steps, and it runs before the steps, which then start warm.
+    def batches(fn):
+        t_end = time.perf_counter() + args.ramp_seconds
+        i = 0
+        while time.perf_counter() < t_end:
+            for _ in range(50):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+        out = []
+        for bi in range(args.batches):
+            hip.record(e0, stream)
+            for j in range(args.batch_launches):
+                fn(i + bi * args.batch_launches + j)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            out.append(hip.ms(e0, e1) / args.batch_launches)
+        return np.array(out), i
+
+    rq_ms, rq_ramp = batches(
+        lambda i: rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream))
+    gemm_ms, gemm_ramp = batches(lambda i: gemm(xq_p, xs_p, wq_ptrs[i % n_w], ws_p, b_ptr, M, N,
+                                                Kp, y_ptrs[i % n_y], None, stream))
+
     for i in range(args.warmup):
         assert step(i) == 0
     torch.cuda.synchronize()
 
-    hip = Hip()
     K_steps = args.steps
     # Timed region: K whole steps back to back, bracketed by a synchronisation on each side
     # (events only at the two ends: an event between kernels costs several microseconds).
-    e0, e1 = hip.event(), hip.event()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     hip.record(e0, stream)
@@ -159,24 +195,6 @@ def gpu_bench(args, wl):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_ms_events = hip.ms(e0, e1) / K_steps
-
-    # Launch duration of each kernel: batches of back-to-back launches of that kernel alone,
-    # on the same inputs (the activations still rotate through the HBM-sized buffer set),
-    # with events around each batch on the launch stream.
-    def batches(fn, n_batches=5, per_batch=max(20, K_steps // 5)):
-        out = []
-        for bi in range(n_batches):
-            hip.record(e0, stream)
-            for i in range(per_batch):
-                fn(bi * per_batch + i)
-            hip.record(e1, stream)
-            torch.cuda.synchronize()
-            out.append(hip.ms(e0, e1) / per_batch)
-        return np.array(out)
-
-    rq_ms = batches(lambda i: rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream))
-    gemm_ms = batches(lambda i: gemm(xq_p, xs_p, wq_ptrs[i % n_w], ws_p, b_ptr, M, N, Kp,
-                                     y_ptrs[i % n_y], None, stream))
     for x in (e0, e1):
         hip.lib.hipEventDestroy(x)
 
@@ -209,6 +227,9 @@ def gpu_bench(args, wl):
         "gemm_tops": gemm_tops, "gemm_ops": ops, "gemm_bytes": gemm_bytes,
         "x_buffers": n_x, "x_buffer_bytes": x_bytes * n_x, "w_buffers": n_w,
         "copy_calibration": copy,
+        "kernel_timing": {"ramp_seconds": args.ramp_seconds, "ramp_launches_rq": rq_ramp,
+                          "ramp_launches_gemm": gemm_ramp, "batches": args.batches,
+                          "launches_per_batch": args.batch_launches},
     }
 
 

@@ -4,7 +4,8 @@ Two uses:
   * ``python -m rotation_w4a4_quantized_convrot_amd.profiling stats <kernel_stats.csv>``
     prints the per-kernel duration table of a ``--kernel-trace --stats`` run, and
     ``... trace <kernel_trace.csv> --last N`` the average over each kernel's last N
-    dispatches (bench.py's back-to-back batches).
+    dispatches, and ``... batches <kernel_trace.csv> --last N`` the average over the last N
+    dispatches of each kernel's longest back-to-back run (bench.py's timed batches).
   * ``python -m rotation_w4a4_quantized_convrot_amd.profiling traffic --fetch <dir>
     --write <dir> --out <file> --command <text>`` turns two ``--pmc FETCH_SIZE`` /
     ``--pmc WRITE_SIZE`` runs of ``bench.py --copy-calibration`` into HBM bytes per launch.
@@ -156,6 +157,31 @@ def trace_tail(path: str, last: int) -> List[dict]:
     return out
 
 
+def trace_batches(path: str, last: int) -> List[dict]:
+    """Average duration of the last `last` dispatches of each kernel's longest run of
+    consecutive dispatches (no other kernel in between): bench.py's back-to-back batches of
+    that kernel alone, wherever they sit in the trace."""
+    rows = []
+    for r in _rows(path):
+        rows.append((int(r["Start_Timestamp"]), r["Kernel_Name"],
+                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    best: Dict[str, List[float]] = {}
+    cur_name, cur = None, []
+    for _, name, dur in rows + [(0, None, 0.0)]:
+        if name != cur_name:
+            if cur_name is not None and len(cur) > len(best.get(cur_name, [])):
+                best[cur_name] = cur
+            cur_name, cur = name, []
+        cur.append(dur)
+    out = []
+    for name, v in best.items():
+        tail = v[-last:]
+        out.append({"name": name, "n": len(tail), "run": len(v), "avg_us": statistics.mean(tail),
+                    "median_us": statistics.median(tail)})
+    return out
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -164,6 +190,9 @@ def main(argv=None) -> int:
     tt = sub.add_parser("trace")
     tt.add_argument("csv")
     tt.add_argument("--last", type=int, required=True)
+    tb = sub.add_parser("batches")
+    tb.add_argument("csv")
+    tb.add_argument("--last", type=int, required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True, nargs="+")
     t.add_argument("--write", required=True, nargs="+")
@@ -178,6 +207,11 @@ def main(argv=None) -> int:
     if a.cmd == "trace":
         for r in trace_tail(a.csv, a.last):
             print(f"{r['n']:6d} last launches  avg {r['avg_us']:9.2f} us  median "
+                  f"{r['median_us']:9.2f} us  {r['name'][:110]}")
+        return 0
+    if a.cmd == "batches":
+        for r in trace_batches(a.csv, a.last):
+            print(f"{r['n']:6d} of {r['run']:6d} back-to-back  avg {r['avg_us']:9.2f} us  median "
                   f"{r['median_us']:9.2f} us  {r['name'][:110]}")
         return 0
     table = traffic(a.fetch, a.write)

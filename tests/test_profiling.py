@@ -52,3 +52,26 @@ def test_calibration_required(tmp_path):
     _write(tmp_path / "w", "WRITE_SIZE", [(GEMM, 55296, 1.0)])
     with pytest.raises(ValueError):
         P.traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+
+
+def test_trace_batches_picks_longest_back_to_back_run(tmp_path):
+    p = tmp_path / "bench_kernel_trace.csv"
+    rows, t = [], 0
+    def add(name, dur_ns):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur_ns})
+        t += dur_ns + 100
+    for _ in range(3):                       # interleaved steps
+        add("A", 5000)
+        add("B", 9000)
+    for _ in range(10):                      # A alone: 10 back to back
+        add("A", 2000)
+    for _ in range(4):
+        add("B", 7000)
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    got = {r["name"]: r for r in P.trace_batches(str(p), 5)}
+    assert got["A"]["run"] == 10 and got["A"]["n"] == 5 and got["A"]["avg_us"] == 2.0
+    assert got["B"]["run"] == 4 and got["B"]["avg_us"] == 7.0
