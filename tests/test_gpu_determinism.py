@@ -45,7 +45,8 @@ def _same_bits(a, b):
 
 GEMM_CASES = [
     # codes, M, N, Kp, kernel chosen by the library for this shape
-    ("int4", 1024, 2048, 512, "tiled"), ("int4", 100, 300, 512, "skinny"),
+    ("int4", 1024, 2048, 512, "tiled"), ("int4", 4000, 4090, 256, "tiled"),
+    ("int4", 100, 300, 512, "skinny"),
     ("int4", 70, 90, 48, "128x128"),
     ("int8", 1024, 2048, 256, "tiled"), ("int8", 100, 300, 512, "skinny"),
     ("mxfp4", 1024, 2048, 512, "tiled"), ("mxfp4", 100, 300, 512, "skinny"),

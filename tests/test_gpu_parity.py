@@ -180,6 +180,8 @@ GEMM_CASES = [
     (300, 7000, 3328, False), (512, 3072, 3072, True), (65, 200, 512, True),
     # large-tile kernel (M N >= 2^21): ragged M and N, several tiles, K tails
     (600, 3500, 512, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
+    (4607, 3071, 128, False), (1130, 1990, 576, True), (4000, 4090, 320, True),
+    (4096, 4096, 128, False),
 ]
 
 
