@@ -37,9 +37,11 @@
  *
  * Memory and threading:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except the host buffer
- *     of convrot_make_rht.  The library never allocates, frees or retains device memory.
- *     Its only global state is a per-device cache of the compute-unit count (atomic);
- *     calls are re-entrant and may come from several host threads.
+ *     of convrot_make_rht.  The library never allocates, frees or retains device memory,
+ *     except the fixed scratch array of convrot_w4a4_linear_noalloc (below), which the
+ *     code object holds on each device it is loaded on.  Its other global state is per-device
+ *     caches of the compute-unit count and of that array's address (atomic); every other
+ *     call is re-entrant and may come from several host threads.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
  *     enqueued asynchronously on it; no call synchronises the device or the stream.  Every
  *     call enqueues kernel launches only (no memset, copy or allocation), so calls may be
@@ -78,7 +80,9 @@ enum {
     CONVROT_ERR_DTYPE = -5,        /* unknown dtype code */
     CONVROT_ERR_ALIGN = -6,        /* a pointer or row stride violates the stated alignment */
     CONVROT_ERR_WORKSPACE = -7,    /* workspace smaller than convrot_w4a4_workspace_bytes() */
-    CONVROT_ERR_HIP = -8           /* the HIP runtime reported an error at launch */
+    CONVROT_ERR_HIP = -8,          /* the HIP runtime reported an error at launch */
+    CONVROT_ERR_SCRATCH = -9       /* convrot_w4a4_linear_noalloc: the problem needs more than
+                                      CONVROT_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /* Element type of activation / weight inputs. */
@@ -254,6 +258,27 @@ CONVROT_API int convrot_mxfp4_linear(const void* x, int32_t x_dtype, int64_t M, 
                                      int64_t g, const uint8_t* wq, const uint8_t* wbs, int64_t N,
                                      const void* bias, void* y, void* workspace, size_t ws_bytes,
                                      void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the ConvLinear4bit forward pass of
+ * convrot_w4a4_linear without a workspace argument.  The packed activation codes and row
+ * scales go to a fixed array of CONVROT_NOALLOC_SCRATCH_BYTES (72 MiB) of device memory inside
+ * the library, one per device, held from the library's first use on that device until the
+ * process ends.  The call allocates and frees nothing (no hipMalloc, no library routine that
+ * allocates); the caller passes inputs and outputs as for convrot_w4a4_linear.
+ *   Limit: convrot_w4a4_workspace_bytes(M, K, g) <= CONVROT_NOALLOC_SCRATCH_BYTES, else
+ *   CONVROT_ERR_SCRATCH before anything is enqueued (e.g. K = 3072, g = 256: M <= 49024).
+ *   Every call on one device shares that device's array, which keeps the last call's codes:
+ *   calls that may overlap in time on one device (several streams, several host threads
+ *   without ordering) race on it and must be serialised by the caller.  Output is identical
+ *   to convrot_w4a4_linear's (the same kernels).
+ * Errors: as convrot_w4a4_linear, with CONVROT_ERR_SCRATCH in place of CONVROT_ERR_WORKSPACE. */
+#define CONVROT_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+
+CONVROT_API int convrot_w4a4_linear_noalloc(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                            int64_t g, const uint8_t* wq, const float* ws,
+                                            int64_t N, const void* bias, void* y, void* stream);
 
 #ifdef __cplusplus
 }

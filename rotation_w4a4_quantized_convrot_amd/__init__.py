@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     convrot_w8a8_linear, convrot_w8a8_workspace_bytes,
     convrot_rotate_quant_act_mxfp4, convrot_quant_weight_mxfp4, convrot_mxfp4_gemm,
     convrot_mxfp4_workspace_bytes, convrot_mxfp4_linear, mx_scale_stride,
+    convrot_w4a4_linear_noalloc, CONVROT_NOALLOC_SCRATCH_BYTES,
 )
 from .linear import ConvLinear4bit, ConvLinear8bit, ConvLinearFP4  # noqa: F401
 
@@ -22,5 +23,5 @@ __all__ = [
     "convrot_w4a4_linear", "convrot_rotate_quant_act_i8", "convrot_quant_weight_i8",
     "convrot_w8a8_gemm", "convrot_w8a8_workspace_bytes", "convrot_w8a8_linear",
     "convrot_rotate_quant_act_mxfp4", "convrot_quant_weight_mxfp4", "convrot_mxfp4_gemm",
-    "convrot_mxfp4_workspace_bytes", "convrot_mxfp4_linear",
+    "convrot_mxfp4_workspace_bytes", "convrot_mxfp4_linear", "convrot_w4a4_linear_noalloc",
 ]

@@ -24,9 +24,11 @@ CONVROT_ERR_DTYPE = -5
 CONVROT_ERR_ALIGN = -6
 CONVROT_ERR_WORKSPACE = -7
 CONVROT_ERR_HIP = -8
+CONVROT_ERR_SCRATCH = -9
 CONVROT_F32 = 0
 CONVROT_BF16 = 1
 CONVROT_MAX_KP = 65536
+CONVROT_NOALLOC_SCRATCH_BYTES = 72 << 20
 
 # (name, restype, argtypes) of every symbol include/convrot.h declares.
 _c_int, _i32, _i64, _vp = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -56,6 +58,8 @@ SIGNATURES = {
     "convrot_mxfp4_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "convrot_mxfp4_linear": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp,
                                       ctypes.c_size_t, _vp]),
+    "convrot_w4a4_linear_noalloc": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp,
+                                             _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -375,6 +379,33 @@ def convrot_w4a4_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Ten
     """ConvLinear4bit forward: x [M, K] contiguous -> y bf16 [M, N]."""
     return _linear(load_library().convrot_w4a4_linear, convrot_w4a4_workspace_bytes, x, g, wq,
                    ws, bias, y, workspace, _half, False)
+
+
+def convrot_w4a4_linear_noalloc(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Tensor,
+                                bias: Optional[torch.Tensor] = None,
+                                y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ConvLinear4bit forward without a workspace: the library keeps the activation codes in a
+    fixed device array of CONVROT_NOALLOC_SCRATCH_BYTES per device (calls that overlap in
+    time on one device race on it).  Pass y to keep the call free of allocations."""
+    M, K = _activations(x, contiguous=True)
+    Kp = convrot_padded_k(K, g)
+    N, cols = _codes_2d(wq, "wq")
+    if cols != Kp // 2:
+        raise ValueError(f"wq must have {Kp // 2} bytes per row for K={K}, g={g} (K' = {Kp}), "
+                         f"got {cols}")
+    _mat(wq, "wq", N, cols, _CODE_BYTES)
+    _is_tensor(ws, "ws")
+    _vec(ws, "ws", N, torch.float32)
+    _vec(bias, "bias", N, torch.bfloat16)
+    _mat(y, "y", M, N, (torch.bfloat16,))
+    dev = _require_device(x, wq, ws, bias, y)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    st = load_library().convrot_w4a4_linear_noalloc(
+        _ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(ws), N, _ptr(bias), _ptr(y),
+        _stream(dev))
+    _check(st, g)
+    return y
 
 
 # ----------------------------------------------------------------- INT8 (W8A8) variant

@@ -3,6 +3,8 @@
 #include "convrot.h"
 #include "convrot_internal.h"
 
+#include <atomic>
+
 namespace {
 
 int pow4_exponent(int64_t g) {
@@ -113,6 +115,10 @@ const char* convrot_status_string(int status) {
     case CONVROT_ERR_ALIGN: return "pointer or row stride violates the required alignment";
     case CONVROT_ERR_WORKSPACE: return "workspace too small";
     case CONVROT_ERR_HIP: return "HIP runtime error at launch";
+    case CONVROT_ERR_SCRATCH:
+      return "the problem needs more scratch than the fixed array of the no-allocation entry "
+             "point (codes M*K'/2 and scales 4*M, each rounded up to 256 bytes, at most "
+             "CONVROT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -359,3 +365,57 @@ int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// No-allocation variant of convrot_w4a4_linear, for callers that cannot allocate device
+// memory.  The packed activation codes and row scales (convrot_w4a4_linear's workspace
+// layout) live in a fixed device array of this file.  In host code the array's name is only a
+// host-side stand-in, so its device address is looked up with hipGetSymbolAddress, once per
+// device with that device current, and kept per device; kernels receive that address.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the device's first call;
+// concurrent first calls look up the same address).
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CONVROT_ERR_HIP;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return CONVROT_ERR_HIP;
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return CONVROT_OK;
+}
+
+}  // namespace
+
+extern "C" int convrot_w4a4_linear_noalloc(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                           int64_t g, const uint8_t* wq, const float* ws,
+                                           int64_t N, const void* bias, void* y, void* stream) {
+  // The same checks as convrot_w4a4_linear, in the same order, up to the workspace; nothing
+  // touches the device before they pass.
+  int st = check_group(g);
+  if (st != CONVROT_OK) return st;
+  if (elem_size(x_dtype) == 0) return CONVROT_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 1 || M > INT32_MAX || N > INT32_MAX) return CONVROT_ERR_SHAPE;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return (int)kp;
+  if (kp > max_row_kp(g, x_dtype)) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (x == nullptr || wq == nullptr || ws == nullptr || y == nullptr) return CONVROT_ERR_NULL;
+  const size_t need = convrot_w4a4_workspace_bytes(M, K, g);
+  if (need > CONVROT_NOALLOC_SCRATCH_BYTES) return CONVROT_ERR_SCRATCH;
+  void* work = nullptr;
+  st = scratch_of_current_device(&work);
+  if (st != CONVROT_OK) return st;
+  // Every byte the GEMM reads is written by rotate+quantize first: nothing to clear.
+  return convrot_w4a4_linear(x, x_dtype, M, K, g, wq, ws, N, bias, y, work,
+                             CONVROT_NOALLOC_SCRATCH_BYTES, stream);
+}

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, -9, -1):
+    for st in range(0, -10, -1):
         assert cr.convrot_status_string(st) not in ("", "unknown status")
     assert cr.convrot_status_string(-99) == "unknown status"
     assert cr.convrot_version() >= 100
@@ -240,3 +240,25 @@ def test_modules_allocate_each_formats_buffers(lib):
     assert tuple(mf.weight_packed.shape) == (N, kp // 2)
     assert tuple(mf.weight_scale.shape) == (N, 4 * (-(-kp // 128)))
     assert str(mf.weight_scale.dtype) == "torch.uint8"
+
+
+def test_noalloc_linear_validates_before_touching_the_device(lib):
+    """The no-allocation entry point checks its arguments, and that the problem fits its fixed
+    scratch array, before any HIP call (these run without a GPU)."""
+    E = _lib
+    call = lambda **k: lib.convrot_w4a4_linear_noalloc(  # noqa: E731
+        k.get("x", A16), k.get("dt", 1), k.get("M", 4), k.get("K", 64), k.get("g", 16),
+        k.get("wq", A16), k.get("ws", A16), k.get("N", 4), k.get("b"), k.get("y", A16), None)
+    assert call(g=8) == E.CONVROT_ERR_GROUP
+    assert call(g=4096) == E.CONVROT_ERR_UNSUPPORTED
+    assert call(dt=7) == E.CONVROT_ERR_DTYPE
+    assert call(M=-1) == E.CONVROT_ERR_SHAPE
+    assert call(x=None) == E.CONVROT_ERR_NULL
+    assert call(M=0, x=None, y=None) == E.CONVROT_OK
+    # K = 3072, g = 256: 1536 code bytes + 4 scale bytes per row (each part 256-byte rounded)
+    limit = _lib.CONVROT_NOALLOC_SCRATCH_BYTES
+    fits = max(m for m in range(49000, 49300)
+               if cr.convrot_w4a4_workspace_bytes(m, 3072, 256) <= limit)
+    assert fits == 49024
+    assert call(M=fits + 1, K=3072, g=256) == E.CONVROT_ERR_SCRATCH
+    assert "no-allocation" in cr.convrot_status_string(E.CONVROT_ERR_SCRATCH)
