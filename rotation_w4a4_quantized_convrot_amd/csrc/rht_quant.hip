@@ -563,21 +563,28 @@ __global__ __launch_bounds__(64 * MW) void rht_quant_kernel(const TIn* __restric
     const bool tiny = mrow > 0.0f && mrow < kQmax * 0x1p-126f;
     const bool any_tiny = __ballot(tiny) != 0;
     const float inv = mrow > 0.0f && !tiny ? kQmax / mrow : 0.0f;
-    const float tiny_scale = tiny ? __fdiv_rn(mrow, kQmax) : 0.0f;
+    float tiny_scale = 0.0f;
+    if (any_tiny) {  // uniform; an opaque copy keeps the division inside the branch
+      float m = mrow;
+      asm volatile("" : "+v"(m));
+      tiny_scale = tiny ? __fdiv_rn(m, kQmax) : 0.0f;
+    }
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       uint32_t bits[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         bits[e] = __float_as_uint(__builtin_fmaf(v[8 * r + e], inv, kMagic));
-      if (any_tiny && tiny) {
+      if (any_tiny) {  // uniform and rarely taken
+        if (tiny) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          bits[e] = __float_as_uint(__fadd_rn(
-              tiny_scale > 0.0f
-                  ? fminf(fmaxf(__fdiv_rn(v[8 * r + e], tiny_scale), -kQmax - 1.0f), kQmax)
-                  : 0.0f,
-              kMagic));
+          for (int e = 0; e < 8; ++e)
+            bits[e] = __float_as_uint(__fadd_rn(
+                tiny_scale > 0.0f
+                    ? fminf(fmaxf(__fdiv_rn(v[8 * r + e], tiny_scale), -kQmax - 1.0f), kQmax)
+                    : 0.0f,
+                kMagic));
+        }
       }
       if constexpr (QB == 4) {
         const uint32_t lo = lshl_or<12>(bits[3], lshl_or<8>(bits[2], lshl_or<4>(bits[1], bits[0])));
