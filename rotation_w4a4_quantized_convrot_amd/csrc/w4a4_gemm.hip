@@ -360,6 +360,28 @@ __device__ __forceinline__ void mma_half(const Half& f, const Half& fs, v16i (&a
   }
 }
 
+// int4 substep operands unpacked ahead of use: the first substep of a stage is unpacked at
+// the end of the previous K step, before its barrier, so that the matrix instructions of the
+// next step can issue as soon as the barrier opens (nothing moves across a barrier).
+struct Unp {
+  v4i w[kGN], x[kGM];
+};
+
+__device__ __forceinline__ void unpack_sub(const Half& f, int s, Unp& u) {
+#pragma unroll
+  for (int i = 0; i < kGN; ++i) u.w[i] = unpack_half(f.w[i], s);
+#pragma unroll
+  for (int j = 0; j < kGM; ++j) u.x[j] = unpack_half(f.x[j], s);
+}
+
+__device__ __forceinline__ void mma_unp(const Unp& u, v16i (&acc)[kGN][kGM]) {
+#pragma unroll
+  for (int i = 0; i < kGN; ++i)
+#pragma unroll
+    for (int j = 0; j < kGM; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(u.w[i], u.x[j], acc[i][j], 0, 0, 0);
+}
+
 // Dequantization epilogue of one 256 x 256 tile.  32x32 accumulator layout: lane l holds
 // column m = l % 32 of a block and, in register r, row n = 8 (r / 4) + 4 (l / 32) + r % 4.
 //   1. The tile's 256 activation scales, weight scales and bias values (loaded into registers
@@ -415,26 +437,16 @@ __device__ __forceinline__ void epi_block(const v16i (&acc)[kGN][kGM], int j, fl
 
 template <bool kDbg, int QB>
 __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, uint8_t* st1,
-                                         uint8_t* st2, uint8_t* st3, float xsv, float wsv,
-                                         uint32_t bbits,
+                                         uint8_t* st2, const float* fx,
                                          int M, int N, long m0, long n0, int wave, int lane,
                                          uint16_t* __restrict__ y,
                                          int32_t* __restrict__ acc_dbg) {
   constexpr int kPitch = 272;
-  float* fx = reinterpret_cast<float*>(st3);
-  float* fw = fx + kBM;
-  float* fb = fw + kBN;
-  const int tid = wave * 64 + lane;
-  if (tid < kBM) {  // kBM == kBN
-    fx[tid] = xsv;
-    fw[tid] = wsv;
-    fb[tid] = __uint_as_float(bbits << 16);  // bf16 -> fp32 is exact
-  }
-  __syncthreads();
-
+  const float* fw = fx + kBM;
+  const float* fb = fw + kBN;
   const int wn = wave & 1, wm = wave >> 1;
   const int r32 = lane & 31;
-  // Each wave's 32 x 128 staging rows: three per stage buffer (st3 holds the factors).
+  // Each wave's 32 x 128 staging rows: three per stage buffer.
   uint8_t* stage = (wave < 3 ? st0 : wave < 6 ? st1 : st2) + (wave % 3) * (32 * kPitch);
   const bool vec16 = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
 #pragma unroll
@@ -482,6 +494,10 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
                        int32_t* __restrict__ acc_dbg) {
   constexpr int kSt = stage_bytes<QB>(), kDpw = dma_per_wave<QB>();
   __shared__ __attribute__((aligned(16))) uint8_t st0[kSt], st1[kSt], st2[kSt], st3[kSt];
+  // The tile's dequantization factors (activation scales, weight scales, bias as fp32),
+  // parked here once the first stage has landed so that no register holds them across the
+  // K loop.
+  __shared__ __attribute__((aligned(16))) float fac[3 * kBM];
 
   // XCD-grouped tile order: blocks are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous range of tiles, walked four tile-rows at a time.
@@ -508,7 +524,7 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
   const int rowB = Kp * code_bits<QB>() / 8;  // bytes of codes per row
   const int srow = ((Kp + 127) >> 7) * 4;       // MXFP4: bytes of block scales per row
   const int nsteps = (rowB + kBKB - 1) / kBKB;
-  // Epilogue factors, loaded now so their latency hides behind the K loop.
+  // Epilogue factors, requested now so that their latency hides behind the first stages.
   float xsv, wsv;
   uint32_t bbits;  // bf16 bits of the bias; -0.0 (0x8000) when there is none
   {
@@ -544,12 +560,22 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
   // transfers.)  The loop is unrolled by four so every buffer is named statically, which
   // lets the compiler keep the newer transfers in flight.
   Half f0, f1, g0;
+  Unp u0;  // int4: substep 0 of the current stage, unpacked before the step's barrier
   issue_stage<QB>(st0, ra, rb, rsa, rsb, rowB, srow, 0, wave, lane);
   issue_stage<QB>(st1, ra, rb, rsa, rsb, rowB, srow, 1, wave, lane);
   issue_stage<QB>(st2, ra, rb, rsa, rsb, rowB, srow, 2, wave, lane);
   __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDpw));  // vmcnt: stage 0 landed
+  {
+    const int tid = wave * 64 + lane;
+    if (tid < kBM) {  // kBM == kBN; the epilogue reads these after the K loop's barriers
+      fac[tid] = xsv;
+      fac[kBM + tid] = wsv;
+      fac[2 * kBM + tid] = __uint_as_float(bbits << 16);  // bf16 -> fp32 is exact
+    }
+  }
   __builtin_amdgcn_s_barrier();
   read_half<QB>(st0, 0, wn, wm, lane, f0);
+  if constexpr (QB == 4) unpack_sub(f0, 0, u0);
 #define CONVROT_STEP(K, CUR, NEXT, REFILL)                                          \
   __builtin_amdgcn_s_waitcnt(0x0F70 | kDpw);        /* vmcnt: stage K + 1 landed */  \
   __builtin_amdgcn_s_waitcnt(0xC07F);               /* lgkmcnt(0) */                \
@@ -557,8 +583,17 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
   issue_stage<QB>(REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);       \
   read_half<QB>(CUR, 1, wn, wm, lane, f1);                                          \
   read_half<QB>(NEXT, 0, wn, wm, lane, g0);                                         \
-  mma_half<QB, 0>(f0, f0, acc);                                                     \
-  mma_half<QB, 1>(f1, f0, acc);                                                     \
+  if constexpr (QB == 4) {                                                          \
+    mma_unp(u0, acc);                                                               \
+    Unp u;                                                                          \
+    unpack_sub(f0, 1, u);                                                           \
+    mma_unp(u, acc);                                                                \
+    mma_half<QB, 1>(f1, f0, acc);                                                   \
+    unpack_sub(g0, 0, u0);                                                          \
+  } else {                                                                          \
+    mma_half<QB, 0>(f0, f0, acc);                                                   \
+    mma_half<QB, 1>(f1, f0, acc);                                                   \
+  }                                                                                 \
   f0 = g0;
   int k = 0;
   for (; k + 4 <= nsteps; k += 4) {
@@ -583,8 +618,7 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
   // buffers are reused.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __builtin_amdgcn_s_barrier();
-  epilogue<kDbg, QB>(acc, st0, st1, st2, st3, xsv, wsv, bbits, M, N, m0, n0, wave, lane, y,
-                 acc_dbg);
+  epilogue<kDbg, QB>(acc, st0, st1, st2, fac, M, N, m0, n0, wave, lane, y, acc_dbg);
 }
 
 }  // namespace big
