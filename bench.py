@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--batches", type=int, default=5)
     p.add_argument("--batch-launches", type=int, default=200,
                    help="launches per timed batch of each kernel")
+    p.add_argument("--fused", action="store_true",
+                   help="int4 only: one step is a single launch of the fused kernel "
+                        "(convrot_w4a4_linear_fused) instead of the two kernels")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0 = all)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -147,6 +150,20 @@ def gpu_bench(args, wl):
                    stream)
         return st
 
+    if args.fused:
+        # one launch per step: the workspace holds the codes and scales; status stays zero
+        # unless the kernel's grid barrier times out (checked after the run)
+        work = torch.empty((cr.convrot_w4a4_workspace_bytes(M, K, g),), dtype=torch.uint8,
+                           device=dev)
+        status = torch.zeros((1,), dtype=torch.int32, device=dev)
+        work_p, status_p, nbytes = work.data_ptr(), status.data_ptr(), work.numel()
+        fused = lib.convrot_w4a4_linear_fused
+
+        def step(i):  # noqa: F811
+            return fused(x_ptrs[i % n_x], dt_code, M, K, g, wq_ptrs[i % n_w], ws_p, N, b_ptr,
+                         y_ptrs[i % n_y], work_p, nbytes, status_p, stream)
+        rq = gemm = None
+
     hip = Hip()
     e0, e1 = hip.event(), hip.event()
 
@@ -174,10 +191,14 @@ def gpu_bench(args, wl):
             out.append(hip.ms(e0, e1) / args.batch_launches)
         return np.array(out), i
 
-    rq_ms, rq_ramp = batches(
-        lambda i: rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream))
-    gemm_ms, gemm_ramp = batches(lambda i: gemm(xq_p, xs_p, wq_ptrs[i % n_w], ws_p, b_ptr, M, N,
-                                                Kp, y_ptrs[i % n_y], None, stream))
+    if args.fused:  # the whole step is one kernel: time it as both
+        gemm_ms, gemm_ramp = batches(step)
+        rq_ms, rq_ramp = gemm_ms, 0
+    else:
+        rq_ms, rq_ramp = batches(
+            lambda i: rq(x_ptrs[i % n_x], dt_code, M, K, K, g, xq_p, xs_p, None, stream))
+        gemm_ms, gemm_ramp = batches(lambda i: gemm(xq_p, xs_p, wq_ptrs[i % n_w], ws_p, b_ptr, M,
+                                                    N, Kp, y_ptrs[i % n_y], None, stream))
 
     for i in range(args.warmup):
         assert step(i) == 0
@@ -195,6 +216,8 @@ def gpu_bench(args, wl):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_ms_events = hip.ms(e0, e1) / K_steps
+    if args.fused:
+        assert int(status.item()) == 0, "the fused kernel's grid barrier timed out"
     for x in (e0, e1):
         hip.lib.hipEventDestroy(x)
 
@@ -295,6 +318,8 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, wl)
     from rotation_w4a4_quantized_convrot_amd import profiling
     i8, mx = args.codes == "int8", args.codes == "mxfp4"
+    if args.fused and (i8 or mx):
+        raise SystemExit("--fused is the int4 layer only")
     # which GEMM kernel the library picks for this shape (see w4a4_gemm.hip)
     rows16 = i8 or (wl.Kp // 2) % 16 == 0
     if mx:
@@ -306,6 +331,8 @@ def main():
     else:
         gemm_kernel, big = "w4a4_gemm_kernel", False
     rq_kernel = "rht_quant_i8" if i8 else "rht_quant_mx4" if mx else "rht_quant_i4"
+    if args.fused:
+        gemm_kernel, rq_kernel, big = "fused_linear", "fused_linear", False
     mfma_peak = FP4_PEAK_TOPS if mx else INT8_PEAK_TOPS
     traffic_file = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     # the recorded counters are for the attention-projection workload's launches
@@ -338,6 +365,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp4" if mx else "i8",
         "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "g": wl.g, "Kp": wl.Kp,
+                   "path": "fused single launch" if args.fused else "rotate+quantize, GEMM",
                    "x_dtype": wl.x_dtype, "bias": wl.bias_std is not None,
                    "x_buffers": r["x_buffers"], "w_buffers": r["w_buffers"]},
         "rotate_quant_GBps": r["rq_gbps"], "rotate_quant_us": r["rq_us"],

@@ -259,6 +259,30 @@ CONVROT_API int convrot_mxfp4_linear(const void* x, int32_t x_dtype, int64_t M, 
                                      const void* bias, void* y, void* workspace, size_t ws_bytes,
                                      void* stream);
 
+/* The ConvLinear4bit forward pass in ONE kernel launch ([PAPER] Abstract: the module
+ * integrates rotation, quantization, GEMM and dequantization): a persistent grid of one
+ * workgroup per compute unit rotates and quantizes x into the workspace, meets at a grid
+ * barrier, then runs the GEMM tiles.  Arguments, workspace layout and results as for
+ * convrot_w4a4_linear (codes, scales and y bit-identical to it), plus
+ *   status   device, uint32, 4-byte aligned; must be 0 on entry.  The kernel sets it to a
+ *            nonzero value if its grid barrier waited 2^20 polls (of the order of a second) (all
+ *            workgroups must be resident at once: another kernel holding compute units can
+ *            delay them); y is then incomplete.  Read it after the stream has finished.
+ * Supported: bf16 x, g = 256 or 1024, K'/2 a multiple of 16 bytes, K even, and one row
+ * within eight waves (K' <= 16384 for g = 256, 32768 for g = 1024); otherwise
+ * CONVROT_ERR_UNSUPPORTED before anything is enqueued.  The barrier keeps its counter in device
+ * memory of the library, one per device: calls that overlap in time on one device must be
+ * serialised by the caller.
+ * Speed: on the attention-projection, MLP down-projection and proj_out layers it takes
+ * 1.15-1.7x the time of convrot_w4a4_linear, since its rotation phase runs at the GEMM's
+ * occupancy (two waves per SIMD) instead of the rotate kernel's; the two-launch path stays
+ * the default and this entry point is the measured alternative.
+ * Errors: as convrot_w4a4_linear, and UNSUPPORTED for the cases above. */
+CONVROT_API int convrot_w4a4_linear_fused(const void* x, int32_t x_dtype, int64_t M, int64_t K,
+                                          int64_t g, const uint8_t* wq, const float* ws,
+                                          int64_t N, const void* bias, void* y, void* workspace,
+                                          size_t ws_bytes, uint32_t* status, void* stream);
+
 /* ---------------------------------------------------------------------------------------
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the ConvLinear4bit forward pass of

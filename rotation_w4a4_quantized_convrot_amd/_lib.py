@@ -60,6 +60,8 @@ SIGNATURES = {
                                       ctypes.c_size_t, _vp]),
     "convrot_w4a4_linear_noalloc": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp,
                                              _vp, _vp]),
+    "convrot_w4a4_linear_fused": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
+                                           _vp, ctypes.c_size_t, _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -379,6 +381,45 @@ def convrot_w4a4_linear(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Ten
     """ConvLinear4bit forward: x [M, K] contiguous -> y bf16 [M, N]."""
     return _linear(load_library().convrot_w4a4_linear, convrot_w4a4_workspace_bytes, x, g, wq,
                    ws, bias, y, workspace, _half, False)
+
+
+def convrot_w4a4_linear_fused(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Tensor,
+                              bias: Optional[torch.Tensor] = None,
+                              y: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None,
+                              status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ConvLinear4bit forward in one kernel launch (rotate + quantize, grid barrier, GEMM):
+    x [M, K] bf16 contiguous -> y bf16 [M, N], bit-identical to convrot_w4a4_linear.
+    status: int32 [1] device tensor, zero on entry; the kernel sets it nonzero if its grid
+    barrier timed out (y then incomplete).  Unsupported shapes raise ConvRotError."""
+    M, K = _activations(x, contiguous=True)
+    Kp = convrot_padded_k(K, g)
+    N, cols = _codes_2d(wq, "wq")
+    if cols != Kp // 2:
+        raise ValueError(f"wq must have {Kp // 2} bytes per row for K={K}, g={g} (K' = {Kp}), "
+                         f"got {cols}")
+    _mat(wq, "wq", N, cols, _CODE_BYTES)
+    _is_tensor(ws, "ws")
+    _vec(ws, "ws", N, torch.float32)
+    _vec(bias, "bias", N, torch.bfloat16)
+    _mat(y, "y", M, N, (torch.bfloat16,))
+    if status is not None:
+        _vec(status, "status", 1, torch.int32)
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _require_device(x, wq, ws, bias, y, workspace, status)
+    if workspace is None:
+        workspace = torch.empty((max(convrot_w4a4_workspace_bytes(M, K, g), 1),),
+                                dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.zeros((1,), dtype=torch.int32, device=dev)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    st = load_library().convrot_w4a4_linear_fused(
+        _ptr(x), _dtype_code(x), M, K, g, _ptr(wq), _ptr(ws), N, _ptr(bias), _ptr(y),
+        _ptr(workspace), _workspace(workspace), _ptr(status), _stream(dev))
+    _check(st, g)
+    return y
 
 
 def convrot_w4a4_linear_noalloc(x: torch.Tensor, g: int, wq: torch.Tensor, ws: torch.Tensor,

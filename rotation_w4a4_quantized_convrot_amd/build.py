@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libconvrot.so")
-SOURCES = ("api.hip", "rht_quant.hip", "w4a4_gemm.hip")
+SOURCES = ("api.hip", "rht_quant.hip", "w4a4_gemm.hip", "fused.hip")
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 anywhere in the device code.

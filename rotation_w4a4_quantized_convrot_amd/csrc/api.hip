@@ -364,6 +364,33 @@ int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
   return status_of(e);
 }
 
+int convrot_w4a4_linear_fused(const void* x, int32_t x_dtype, int64_t M, int64_t K, int64_t g,
+                              const uint8_t* wq, const float* ws, int64_t N, const void* bias,
+                              void* y, void* workspace, size_t ws_bytes, uint32_t* status,
+                              void* stream) {
+  int st = check_group(g);
+  if (st != CONVROT_OK) return st;
+  if (elem_size(x_dtype) == 0) return CONVROT_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 1 || M > INT32_MAX || N > INT32_MAX) return CONVROT_ERR_SHAPE;
+  const int64_t kp = convrot_padded_k(K, g);
+  if (kp < 0) return (int)kp;
+  if (kp > max_row_kp(g, x_dtype)) return CONVROT_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return CONVROT_OK;
+  if (!convrot::fused_linear_supported(x_dtype, (int)g, M, N, K, kp)) return CONVROT_ERR_UNSUPPORTED;
+  if (x == nullptr || wq == nullptr || ws == nullptr || y == nullptr || workspace == nullptr ||
+      status == nullptr)
+    return CONVROT_ERR_NULL;
+  if (!aligned(workspace, 256) || !aligned(x, 4) || !aligned(status, 4)) return CONVROT_ERR_ALIGN;
+  if (ws_bytes < convrot_w4a4_workspace_bytes(M, K, g)) return CONVROT_ERR_WORKSPACE;
+  uint8_t* xq = static_cast<uint8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(xq + round256((size_t)M * (size_t)(kp / 2)));
+  st = validate_gemm(xq, xs, wq, ws, bias, M, N, kp, y, nullptr);
+  if (st != CONVROT_OK) return st;
+  return status_of(convrot::launch_fused_linear(
+      x, M, K, (int)g, kp, xq, xs, wq, ws, static_cast<const uint16_t*>(bias), N,
+      static_cast<uint16_t*>(y), status, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------

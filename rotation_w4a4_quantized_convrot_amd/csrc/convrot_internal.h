@@ -41,6 +41,18 @@ hipError_t launch_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_
                              const uint8_t* wbs, const uint16_t* bias, int64_t M, int64_t N,
                              int64_t Kp, uint16_t* y, float* acc_dbg, hipStream_t stream);
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+
+// The fused single-launch ConvLinear4bit (bf16 rows, g = 256 or 1024, int4 codes): whether a
+// shape is supported, and the launch.  xq / xs: the workspace's codes and scales; fail: a word
+// of device memory that the kernel sets to nonzero if its grid barrier timed out.
+bool fused_linear_supported(int x_dtype, int g, int64_t M, int64_t N, int64_t K, int64_t Kp);
+hipError_t launch_fused_linear(const void* x, int64_t M, int64_t K, int g, int64_t Kp,
+                               uint8_t* xq, float* xs, const uint8_t* wq, const float* ws,
+                               const uint16_t* bias, int64_t N, uint16_t* y, unsigned* fail,
+                               hipStream_t stream);
+
 // Small launch helper that returns the launch status instead of relying on hipGetLastError.
 template <typename... KArgs, typename... Args>
 inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,

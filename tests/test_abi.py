@@ -262,3 +262,22 @@ def test_noalloc_linear_validates_before_touching_the_device(lib):
     assert fits == 49024
     assert call(M=fits + 1, K=3072, g=256) == E.CONVROT_ERR_SCRATCH
     assert "no-allocation" in cr.convrot_status_string(E.CONVROT_ERR_SCRATCH)
+
+
+def test_fused_linear_validates_before_launch(lib):
+    """convrot_w4a4_linear_fused refuses what its single kernel does not implement, before
+    any device call (no GPU needed)."""
+    E = _lib
+    call = lambda **k: lib.convrot_w4a4_linear_fused(  # noqa: E731
+        k.get("x", A16), k.get("dt", 1), k.get("M", 4), k.get("K", 3072), k.get("g", 256),
+        k.get("wq", A16), k.get("ws", A16), k.get("N", 4), k.get("b"), k.get("y", A16),
+        k.get("wsp", A16 * 16), k.get("nbytes", 1 << 20), k.get("status", A16), None)
+    assert call(g=8) == E.CONVROT_ERR_GROUP
+    assert call(g=64) == E.CONVROT_ERR_UNSUPPORTED         # window sizes 256 and 1024 only
+    assert call(dt=0) == E.CONVROT_ERR_UNSUPPORTED         # bf16 rows only
+    assert call(K=3071) == E.CONVROT_ERR_UNSUPPORTED       # odd rows are not dword aligned
+    assert call(K=17000) == E.CONVROT_ERR_UNSUPPORTED      # a row beyond eight waves
+    assert call(status=None) == E.CONVROT_ERR_NULL
+    assert call(wsp=A16 * 16 + 16) == E.CONVROT_ERR_ALIGN
+    assert call(nbytes=cr.convrot_w4a4_workspace_bytes(4, 3072, 256) - 1) == E.CONVROT_ERR_WORKSPACE
+    assert call(M=0, x=None, y=None) == E.CONVROT_OK
