@@ -470,6 +470,237 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
 
 }  // namespace skinny
 
+// ---------------------------------------------------------------------------------------
+// Skinny kernel with LDS staging, for int4 codes and at most 64 activation rows (decode-like
+// M).  A workgroup owns 32 output columns x 32 activation rows, as the 32-row skinny form
+// does, but its operands arrive by buffer loads straight into LDS in whole 128-byte lines:
+// each 1 KB transfer is eight rows x one line, where the register form's 16-byte loads touch
+// 32 rows per instruction.  At this size the kernel is bound by how fast a compute unit pulls
+// its 96 KB, and whole-line transfers pull it faster (measured on MI355X, M = 64,
+// N = K' = 3072, back to back in a HIP graph: 5.9 against 6.6 us with the weights streamed
+// from HBM, 4.7 against 5.5 us from L2; K' = 12288: 14.4 against 17.9 us).
+//   * K goes in rounds of 1 KB of codes per row (16 K steps, one per wave), double-buffered:
+//     round r + 2 is requested into a buffer once every wave has finished reading round r.
+//   * LDS holds a round as [operand][line][row][128 B]; 16-byte slot p of row r holds chunk
+//     p ^ (r % 8) of the line, so the fragment reads (eight consecutive rows, one chunk)
+//     hit eight different slots.
+//   * Fragments, unpacking and the K order are those of the other kernels; the waves'
+//     partial sums meet in LDS (the round buffers' space) and are added in wave order, which
+//     for integer sums is exact.
+namespace skinny_lds {
+
+using big::v16i;
+using big::f32x2;
+using big::bf16x2;
+constexpr int kTN = 32, kTM = 32;         // output columns and activation rows per workgroup
+constexpr int kWaves = 16, kThreads = 64 * kWaves;
+constexpr int kRB = 1024;                 // bytes of codes per row per round
+constexpr int kOp = kTN * kRB;            // one operand of a round: 32 rows, 32 KB
+constexpr int kBuf = 2 * kOp;             // a round: weights, then activations
+constexpr int kTransfers = 2 * kOp / 1024 / kWaves;  // 1 KB transfers per wave per round (4)
+
+// Round transfers into one round buffer: transfer t = wave + 16 i; i < 2 are weights, i >= 2
+// activations; within an operand, line t % 32 / 4 and rows 8 (t % 4) .. + 7.  Bytes past the
+// row (and rows past M or N, through the buffer range) arrive as zeros.
+__device__ __forceinline__ void issue_round(uint8_t* __restrict__ buf, __amdgpu_buffer_rsrc_t rw,
+                                            __amdgpu_buffer_rsrc_t rx, int rowB, int kb0,
+                                            int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < kTransfers; ++i) {
+    const int t = (wave + kWaves * i) & 31;
+    const int L = t >> 2, rg = t & 3;
+    const int r = 8 * rg + (lane >> 3), c = (lane & 7) ^ (r & 7);
+    const int byte = kb0 + 128 * L + 16 * c;
+    const uint32_t off = byte < rowB ? uint32_t(r * rowB + byte) : big::kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        i < kTransfers / 2 ? rw : rx,
+        (big::lds_ptr)(buf + (i < kTransfers / 2 ? 0 : kOp) + 4096 * L + 1024 * rg),
+        16, off, 0, 0, 0);
+  }
+}
+
+// 16-byte chunk q (0..3) of K step s of the round, row r of one operand.
+__device__ __forceinline__ uint4 frag(const uint8_t* op, int s, int q, int r) {
+  const int c = 4 * (s & 1) + q;
+  return *reinterpret_cast<const uint4*>(op + 4096 * (s >> 1) + 128 * r + 16 * (c ^ (r & 7)));
+}
+
+// This wave's K step of the round in buf (wave w takes step w).
+__device__ __forceinline__ void mma_round(const uint8_t* __restrict__ buf, int rowB, int kb0, int wave,
+                                          int lane, v16i& acc) {
+  const int nst = min(kWaves, (rowB - kb0 + kBKB - 1) / kBKB);
+  if (wave >= nst) return;
+  const int r32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint4 w = frag(buf, wave, 2 * h + c, r32), x = frag(buf + kOp, wave, 2 * h + c, r32);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(big::unpack_half(w, s), big::unpack_half(x, s),
+                                                  acc, 0, 0, 0);
+  }
+}
+
+// Barriers of the round loop.  A fenced __syncthreads would also wait for the transfers of the
+// next round; instead each wave waits for its own transfers of the round about to be read
+// (vector memory counter at most VM: the operations issued after them) and a plain s_barrier
+// makes every wave's transfers visible.  The empty asm statements keep the compiler from
+// moving LDS accesses across the barrier.
+template <int VM>
+__device__ __forceinline__ void round_ready() {
+  __builtin_amdgcn_s_waitcnt(0x0F70 | VM);  // vmcnt(VM); expcnt, lgkmcnt: no wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Every wave's LDS reads are done (its fragments are in registers): the buffer may be refilled.
+__device__ __forceinline__ void buffer_free() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The kernel body, inlined into the kernel (two separate LDS arrays for the round buffers).
+template <bool kDbg>
+__device__ __forceinline__ void skinny_lds_body(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
+    const float* __restrict__ ws, const uint16_t* __restrict__ bias, int M, int N, int Kp,
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg, uint8_t* buf0, uint8_t* buf1) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long n0 = (long)blockIdx.x * kTN, m0 = (long)blockIdx.y * kTM;
+  const int rowB = Kp / 2;
+  const long nw = min(long(N) - n0, long(kTN)), mx = min(long(M) - m0, long(kTM));
+  const __amdgpu_buffer_rsrc_t rw = big::rsrc(wq + n0 * rowB, nw * rowB);
+  const __amdgpu_buffer_rsrc_t rx = big::rsrc(xq + m0 * rowB, mx * rowB);
+  const int nrounds = (rowB + kRB - 1) / kRB;
+  // Rounds 0 and 1 first (round 1 is all zeros when the row is shorter), then the
+  // dequantization factors of this thread's four outputs (row l % 32, columns
+  // 8 g + 4 (l / 32) .. + 3): nine loads per wave, used only by the epilogue.
+  issue_round(buf0, rw, rx, rowB, 0, wave, lane);
+  issue_round(buf1, rw, rx, rowB, kRB, wave, lane);
+  const __amdgpu_buffer_rsrc_t rxs = big::rsrc(xs + m0, mx * 4);
+  const __amdgpu_buffer_rsrc_t rws = big::rsrc(ws + n0, nw * 4);
+  const __amdgpu_buffer_rsrc_t rbs = big::rsrc(bias != nullptr ? bias + n0 : nullptr,
+                                               bias != nullptr ? nw * 2 : 0);
+  const int l = tid & 63, g = (tid >> 6) & 3;
+  const long m = m0 + (l & 31), n = n0 + 8 * g + 4 * (l >> 5);
+  const bool live = tid < 256 && m < M;
+  const float fsx = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(rxs, live ? uint32_t((m - m0) * 4) : big::kOob,
+                                                  0, 0));
+  float fw[4];
+  uint32_t fb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const bool in = live && n + r < N;
+    fw[r] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rws, in ? uint32_t((n - n0 + r) * 4) : big::kOob,
+                                                    0, 0));
+    fb[r] = __builtin_bit_cast(
+        unsigned short, __builtin_amdgcn_raw_buffer_load_b16(
+                            rbs, in ? uint32_t((n - n0 + r) * 2) : big::kOob, 0, 0));
+  }
+
+  // Waits count this wave's vector memory operations, which complete in issue order: a round
+  // is here once at most the operations issued after it are outstanding (for round 0 the
+  // four of round 1 and the nine factor loads; later, the four of the next round if it was
+  // requested).
+  v16i acc = v16i{};
+  for (int rd = 0; rd < nrounds; rd += 2) {
+    if (rd == 0)
+      round_ready<13>();
+    else if (rd + 1 < nrounds)
+      round_ready<4>();
+    else
+      round_ready<0>();
+    mma_round(buf0, rowB, rd * kRB, wave, lane, acc);
+    if (rd + 2 < nrounds) {
+      buffer_free();
+      issue_round(buf0, rw, rx, rowB, (rd + 2) * kRB, wave, lane);
+    }
+    if (rd + 1 >= nrounds) break;
+    if (rd + 2 < nrounds)
+      round_ready<4>();
+    else
+      round_ready<0>();
+    mma_round(buf1, rowB, (rd + 1) * kRB, wave, lane, acc);
+    if (rd + 3 < nrounds) {
+      buffer_free();
+      issue_round(buf1, rw, rx, rowB, (rd + 3) * kRB, wave, lane);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the factors (and round 1 when it was not read)
+  __syncthreads();                // every wave is done reading buffer 0
+  int32_t* red = reinterpret_cast<int32_t*>(buf0);   // 16 waves x 16 x 64 sums: 64 KB
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+  __syncthreads();
+
+  // Final sums and dequantization, four consecutive columns per thread (32x32 accumulator
+  // layout: lane l holds row l % 32 and, in register r, column 8 (r / 4) + 4 (l / 32) + r % 4).
+  if (tid >= 256 || m >= M || n >= N) return;
+  float z[4];
+  int32_t t[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int32_t a = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) a += red[(w * 16 + 4 * g + r) * 64 + l];
+    t[r] = a >> 8;  // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
+    // bf16 -> fp32 is exact; a missing bias is -0.0, an exact identity for the add
+    const float bv = bias != nullptr ? __uint_as_float(fb[r] << 16) : -0.0f;
+    z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], fsx), fw[r]), bv);
+  }
+  const bf16x2 lo = __builtin_convertvector((f32x2){z[0], z[1]}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){z[2], z[3]}, bf16x2);
+  uint16_t* yp = y + m * (long)N + n;
+  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0) {
+    *reinterpret_cast<uint2*>(yp) =
+        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+  } else {
+    const uint16_t o[4] = {uint16_t(__builtin_bit_cast(uint32_t, lo)),
+                           uint16_t(__builtin_bit_cast(uint32_t, lo) >> 16),
+                           uint16_t(__builtin_bit_cast(uint32_t, hi)),
+                           uint16_t(__builtin_bit_cast(uint32_t, hi) >> 16)};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) yp[r] = o[r];
+  }
+  if (kDbg) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < N) acc_dbg[m * (long)N + n + r] = t[r];
+  }
+}
+
+template <bool kDbg>
+__global__ __launch_bounds__(kThreads) void quant_gemm_skinny_lds_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
+    const float* __restrict__ ws, const uint16_t* __restrict__ bias, int M, int N, int Kp,
+    uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBuf];  // two round buffers of 64 KB
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[kBuf];
+  skinny_lds_body<kDbg>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, buf0, buf1);
+}
+
+}  // namespace skinny_lds
+
+hipError_t launch_skinny_lds(const uint8_t* xq, const float* xs, const uint8_t* wq,
+                             const float* ws, const uint16_t* bias, int64_t M, int64_t N,
+                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
+  const dim3 grid(unsigned((N + skinny_lds::kTN - 1) / skinny_lds::kTN),
+                  unsigned((M + skinny_lds::kTM - 1) / skinny_lds::kTM));
+  const dim3 block(skinny_lds::kThreads);
+  if (acc_dbg != nullptr)
+    return launch_kernel(skinny_lds::quant_gemm_skinny_lds_kernel<true>, grid, block, 0, stream,
+                         xq, xs, wq, ws, bias, int(M), int(N), int(Kp), y, acc_dbg);
+  return launch_kernel(skinny_lds::quant_gemm_skinny_lds_kernel<false>, grid, block, 0, stream,
+                       xq, xs, wq, ws, bias, int(M), int(N), int(Kp), y, acc_dbg);
+}
+
 template <int QB, int MB>
 hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* wq,
                             const float* ws, const uint8_t* xbs, const uint8_t* wbs,
@@ -487,6 +718,8 @@ hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* w
 // Largest M routed to the skinny kernel, per code format (measured on MI355X at N = K' = 3072:
 // int4 and MXFP4 against the tiled kernel of the same format).
 constexpr int64_t kSkinnyMaxM4 = 512, kSkinnyMaxM8 = 256, kSkinnyMaxMx = 256;
+// Largest M routed to the LDS-staged int4 skinny kernel.
+constexpr int64_t kSkinnyLdsMaxM = 64;
 
 // A dispatch counts its work-items in 32-bit fields.  The skinny grid has N / 32 workgroups
 // of up to 1024 threads, so it fits only below about N = 2^27; wider outputs take another
@@ -545,6 +778,10 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
   const bool rows16 = (Kp / 2) % 16 == 0;  // 16-byte packed rows
   // Few activation rows: 256 x 256 tiles would leave most CUs idle (measured on MI355X at
   // N = 3072: the skinny kernel is faster up to M = 512).
+  // Up to 64 rows: operands staged through LDS in whole lines (same grid as the 32-row
+  // skinny form).
+  if (rows16 && M <= kSkinnyLdsMaxM && skinny_fits(M, N))
+    return launch_skinny_lds(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   if (rows16 && M <= kSkinnyMaxM4 && skinny_fits(M, N))
     return launch_skinny<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   // The large tile needs 16-byte packed rows and enough work to fill the chip (or an output

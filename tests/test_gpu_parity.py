@@ -178,6 +178,9 @@ GEMM_CASES = [
     (1, 40, 128, True), (128, 128, 128, False), (200, 136, 1024, True), (129, 130, 256, True),
     (300, 257, 3072, False), (64, 256, 3328, True), (33, 96, 12288, False),
     (300, 7000, 3328, False), (512, 3072, 3072, True), (65, 200, 512, True),
+    # M <= 64 (LDS-staged skinny kernel): one partial round with ragged N, exactly two
+    # rounds, three rounds (an odd count, the last one half full), eight rounds
+    (63, 2, 1056, True), (32, 33, 4096, False), (64, 3000, 5120, True), (40, 1000, 16384, False),
     # large-tile kernel (M N >= 2^21): ragged M and N, several tiles, K tails
     (600, 3500, 512, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
     (4607, 3071, 128, False), (1130, 1990, 576, True), (4000, 4090, 320, True),
