@@ -1,0 +1,111 @@
+"""Matrix-core rate and shader clock of the GPU, measured with libconvrot_calib.so.
+
+``python -m rotation_w4a4_quantized_convrot_amd.calibration [--out FILE]`` runs the
+MFMA-only kernel (v_mfma_i32_32x32x32_i8 in four independent chains per wave, nothing else in
+flight) at one, two and four waves per SIMD, one workgroup per compute unit, each launch about
+0.15 s long, and reports for each:
+  * the int8 rate in POP/s (two ops per multiply-accumulate) and its fraction of MI355X's
+    published dense int8 peak, 5.0 POP/s;
+  * the shader clock while the loop ran: for every workgroup, shader clock cycles
+    (s_memtime) over the 100 MHz real-time counter (s_memrealtime) between the same two
+    points; median, minimum and maximum over the workgroups.
+The published peak assumes 2.4 GHz; at a lower sustained clock the reachable rate scales
+with it, which is what the clock column is for.  Needs a GPU; loads only the calibration
+library (the oracle and the layer's library are not involved).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import os
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CALIB_PATH = os.path.join(PKG, "libconvrot_calib.so")
+PEAK_INT8_POPS = 5.0e15
+PEAK_CLOCK_HZ = 2.4e9
+REALTIME_HZ = 100e6
+
+
+def load() -> ctypes.CDLL:
+    if not os.path.exists(CALIB_PATH):
+        raise RuntimeError(f"{CALIB_PATH} is not built (python -m "
+                           "rotation_w4a4_quantized_convrot_amd.build)")
+    lib = ctypes.CDLL(CALIB_PATH)
+    lib.convrot_calib_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.convrot_calib_mfma_i8.restype = ctypes.c_int
+    lib.convrot_calib_macs_per_mfma.restype = ctypes.c_int64
+    lib.convrot_calib_chains.restype = ctypes.c_int
+    return lib
+
+
+def run(lib, grid: int, block: int, iters: int) -> dict:
+    """One timed launch; returns its POP/s and the per-workgroup clocks in Hz."""
+    import torch
+    sink = torch.empty(grid * block, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(4 * grid, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    rc = lib.convrot_calib_mfma_i8(grid, block, iters, ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(clocks.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"convrot_calib_mfma_i8 failed: hipError {rc}")
+    b.record(stream)
+    b.synchronize()
+    sec = a.elapsed_time(b) / 1e3
+    ops = 2 * lib.convrot_calib_macs_per_mfma() * lib.convrot_calib_chains() * iters * grid * (block // 64)
+    c = clocks.view(grid, 4).cpu().tolist()
+    hz = [(t1 - t0) / ((r1 - r0) / REALTIME_HZ) for t0, t1, r0, r1 in c if r1 > r0]
+    return {"sec": sec, "pops": ops / sec, "sclk_hz": hz}
+
+
+def measure(target_sec: float = 0.15) -> list:
+    import torch
+    lib = load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for waves in (1, 2, 4):
+        block = 256 * waves
+        run(lib, cus, block, 1000)                              # warm-up
+        probe = run(lib, cus, block, 20000)
+        iters = max(1000, int(20000 * target_sec / probe["sec"]))
+        r = run(lib, cus, block, iters)
+        hz = r["sclk_hz"]
+        out.append({"waves_per_simd": waves, "grid": cus, "block": block, "iters": iters,
+                    "ms": r["sec"] * 1e3, "pops": r["pops"], "frac": r["pops"] / PEAK_INT8_POPS,
+                    "sclk_ghz_median": statistics.median(hz) / 1e9,
+                    "sclk_ghz_min": min(hz) / 1e9, "sclk_ghz_max": max(hz) / 1e9})
+    return out
+
+
+def main(argv=None) -> int:
+    p = argparse.ArgumentParser()
+    p.add_argument("--out", default=None, help="write the summary here as well")
+    p.add_argument("--command", default="python -m rotation_w4a4_quantized_convrot_amd.calibration")
+    a = p.parse_args(argv)
+    import torch
+    rows = measure()
+    name = torch.cuda.get_device_properties(0).name
+    lines = ["# MFMA-only rate of v_mfma_i32_32x32x32_i8 (4 independent chains per wave, one "
+             "workgroup per CU) and the shader clock under it",
+             "# sclk = s_memtime cycles / s_memrealtime (100 MHz) per workgroup; frac = POP/s / "
+             "5.0e15 (published dense int8 peak at 2.4 GHz)",
+             f"# command (repository root): {a.command}",
+             f"device={name}; cus={rows[0]['grid']}"]
+    for r in rows:
+        lines.append("; ".join(f"{k}={v:.4g}" if isinstance(v, float) else f"{k}={v}"
+                               for k, v in r.items()))
+    text = "\n".join(lines) + "\n"
+    print(text, end="")
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

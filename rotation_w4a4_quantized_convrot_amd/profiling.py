@@ -11,8 +11,14 @@ Two uses:
     ``--pmc WRITE_SIZE`` runs of ``bench.py --copy-calibration`` into HBM bytes per launch.
     Each counter is scaled by what it reads for a plain elementwise copy of known size
     (256 MiB read, 256 MiB written) run in the same process.  The summary records the
-    SHA-256 of each kernel's source file, so a reader (bench.py) can tell whether the
+    SHA-256 of each kernel's source files, so a reader (bench.py) can tell whether the
     kernel has changed since the counters were taken.
+  * ``python -m rotation_w4a4_quantized_convrot_amd.profiling counters --pmc <dir> ...
+    --stats <kernel_stats.csv> --out <file>`` summarises ``--pmc`` runs of bench.py and of
+    the MFMA-only calibration kernel (calibration.py): per-dispatch counter values of the
+    GEMM, the rotate+quantize kernel and the calibration kernel, and what follows from them
+    (matrix-core busy fraction relative to the MFMA-only kernel, MFMA instructions against
+    the count the tile shape implies, VALU / SALU / LDS instructions per element).
 
 Nothing here touches the GPU; it only reads files.
 """
@@ -29,20 +35,30 @@ from typing import Dict, List, Optional
 PKG = os.path.dirname(os.path.abspath(__file__))
 CALIBRATION_BYTES = 256 << 20          # bench.py --copy-calibration: bytes read and written
 
-# kernel key -> (substring of the demangled name, source file under csrc/)
+# The files a kernel's device code comes from (the kernel source and the headers holding its
+# body), hashed together.
+GEMM_SRC = ("w4a4_gemm.hip", "gemm_device.h", "convrot_internal.h")
+RQ_SRC = ("rht_quant.hip", "rht_quant_device.h", "convrot_internal.h")
+
+# kernel key -> (substring of the demangled name, source files under csrc/)
 KERNELS = {
-    "w4a4_gemm": ("quant_gemm_kernel<false, 4>", "w4a4_gemm.hip"),
-    "w8a8_gemm": ("quant_gemm_kernel<false, 8>", "w4a4_gemm.hip"),
-    "rht_quant_i4": ("rht_quant_kernel<256, unsigned short, 16, 4", "rht_quant.hip"),
-    "rht_quant_i8": ("rht_quant_kernel<256, unsigned short, 16, 8", "rht_quant.hip"),
-    "rht_quant_mx4": ("rht_quant_kernel<256, unsigned short, 16, 1", "rht_quant.hip"),
-    "mxfp4_gemm": ("quant_gemm_kernel<false, 1>", "w4a4_gemm.hip"),
+    "w4a4_gemm": ("quant_gemm_kernel<false, 4>", GEMM_SRC),
+    "w8a8_gemm": ("quant_gemm_kernel<false, 8>", GEMM_SRC),
+    "rht_quant_i4": ("rht_quant_kernel<256, unsigned short, 16, 4", RQ_SRC),
+    "rht_quant_i8": ("rht_quant_kernel<256, unsigned short, 16, 8", RQ_SRC),
+    "rht_quant_mx4": ("rht_quant_kernel<256, unsigned short, 16, 1", RQ_SRC),
+    "mxfp4_gemm": ("quant_gemm_kernel<false, 1>", GEMM_SRC),
 }
+CALIB_KERNEL = "mfma_i8_loop"
 
 
-def source_sha256(src: str) -> str:
-    with open(os.path.join(PKG, "csrc", src), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha256(src) -> str:
+    """SHA-256 of one source file under csrc/, or of several concatenated in order."""
+    h = hashlib.sha256()
+    for name in ((src,) if isinstance(src, str) else src):
+        with open(os.path.join(PKG, "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _rows(path: str) -> List[dict]:
@@ -132,6 +148,101 @@ def read_traffic(path: str, key: str) -> Optional[dict]:
     return None
 
 
+def counter_medians(dirs: List[str], needle: str) -> Dict[str, float]:
+    """Median per-dispatch value of every counter in the ``--pmc`` runs under `dirs`, over the
+    dispatches of the kernel whose name contains `needle` (the first dispatch of each run,
+    with cold caches, left out when there are several)."""
+    out: Dict[str, float] = {}
+    for d in dirs:
+        per: Dict[str, List[float]] = {}
+        for r in _rows(_counter_file(d)):
+            if needle in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for name, vals in per.items():
+            out[name] = statistics.median(vals[1:] if len(vals) > 1 else vals)
+    return out
+
+
+def counters_of_largest(dirs: List[str], needle: str, by: str) -> Dict[str, float]:
+    """Every counter of the one dispatch (per run) of the kernel whose name contains `needle`
+    with the largest value of counter `by` (calibration.py's timed launch of its last
+    configuration is the longest one)."""
+    out: Dict[str, float] = {}
+    for d in dirs:
+        per: Dict[str, Dict[str, float]] = {}
+        for r in _rows(_counter_file(d)):
+            if needle in r["Kernel_Name"]:
+                per.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        if per:
+            out.update(max(per.values(), key=lambda c: c.get(by, 0.0)))
+    return out
+
+
+def read_calibration(path: str) -> Dict[int, dict]:
+    """calibration.py's summary: waves per SIMD -> {pops, sclk_ghz_median, ...}."""
+    out = {}
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("waves_per_simd="):
+                continue
+            d = {}
+            for part in line.strip().split("; "):
+                k, _, v = part.partition("=")
+                d[k] = float(v)
+            out[int(d["waves_per_simd"])] = d
+    return out
+
+
+def counter_summary(pmc_dirs: List[str], calib_dirs: List[str], stats_csv: str,
+                    calib_txt: str, M: int, N: int, Kp: int, cus: int) -> List[str]:
+    """Text lines: raw counter values per kernel and what follows from them."""
+    gemm = counter_medians(pmc_dirs, KERNELS["w4a4_gemm"][0])
+    rq = counter_medians(pmc_dirs, KERNELS["rht_quant_i4"][0])
+    cal = counters_of_largest(calib_dirs, CALIB_KERNEL, "SQ_INSTS_MFMA")
+    peak = read_calibration(calib_txt)[2]          # two waves per SIMD, as the GEMM runs
+    dur = {}
+    for r in kernel_stats(stats_csv):
+        for key in ("w4a4_gemm", "rht_quant_i4"):
+            if KERNELS[key][0] in r["name"]:
+                dur[key] = r["avg_us"]
+    lines = []
+    for label, d in (("w4a4_gemm", gemm), ("rht_quant_i4", rq), ("mfma_only", cal)):
+        lines.append(f"raw kernel={label}; " + "; ".join(f"{k}={v:.6g}" for k, v in sorted(d.items())))
+    lines.append(f"calibration (2 waves per SIMD): MFMA-only {peak['pops'] / 1e15:.4g} POP/s at "
+                 f"sclk {peak['sclk_ghz_median']:.4g} GHz (median over workgroups)")
+    if "SQ_INSTS_MFMA" in gemm:
+        expect = (-(-M // 32)) * (-(-N // 32)) * (Kp // 32)
+        lines.append(f"derived w4a4_gemm mfma_insts={gemm['SQ_INSTS_MFMA']:.7g} expected={expect} "
+                     "(one v_mfma_i32_32x32x32_i8 per 32x32 output block per 32 codes of K')")
+    for label, d in (("w4a4_gemm", gemm), ("mfma_only", cal)):
+        if d.get("SQ_INSTS_MFMA"):
+            lines.append(f"derived {label} mfma_busy_cycles_per_mfma="
+                         f"{d['SQ_VALU_MFMA_BUSY_CYCLES'] / d['SQ_INSTS_MFMA']:.4g}")
+    lines.append("note: SQ_VALU_MFMA_BUSY_CYCLES adds the same fixed amount per instruction in both "
+                 "kernels, so it counts instructions, not time; the matrix cores' busy fraction is "
+                 "the achieved rate over the MFMA-only rate at the same occupancy")
+    if "w4a4_gemm" in dur:
+        pops = 2.0 * M * N * Kp / (dur["w4a4_gemm"] * 1e-6)
+        lines.append(f"derived w4a4_gemm kernel_us={dur['w4a4_gemm']:.4g} pops={pops / 1e15:.4g} "
+                     f"mfma_busy_fraction={pops / peak['pops']:.4f} (of the MFMA-only rate) "
+                     f"frac_of_published={pops / 5.0e15:.4f}")
+    elems = M * Kp
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD",
+              "SQ_INSTS_VMEM_WR", "SQ_INSTS_BRANCH"):
+        if c in rq:
+            lines.append(f"derived rht_quant_i4 {c}_per_element={rq[c] * 64 / elems:.4g} "
+                         f"(wave instructions x 64 lanes / (M x K' = {elems}))")
+    if "rht_quant_i4" in dur and rq.get("SQ_INSTS_VALU"):
+        # 16-lane SIMDs: a wave64 VALU instruction holds its SIMD four cycles, so a CU issues at
+        # most one per cycle
+        cyc = cus * dur["rht_quant_i4"] * 1e-6 * peak["sclk_ghz_median"] * 1e9
+        lines.append(f"derived rht_quant_i4 kernel_us={dur['rht_quant_i4']:.4g} "
+                     f"valu_issue_fraction={rq['SQ_INSTS_VALU'] / cyc:.4f} (VALU instructions over "
+                     "CU cycles at the calibrated clock; one wave64 VALU instruction per CU per "
+                     "cycle at most)")
+    return lines
+
+
 def kernel_stats(path: str) -> List[dict]:
     out = []
     for r in _rows(path):
@@ -198,7 +309,27 @@ def main(argv=None) -> int:
     t.add_argument("--write", required=True, nargs="+")
     t.add_argument("--out", required=True)
     t.add_argument("--command", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("--pmc", required=True, nargs="+", help="--pmc runs of bench.py")
+    c.add_argument("--calib", required=True, nargs="+", help="--pmc runs of calibration.py")
+    c.add_argument("--stats", required=True, help="kernel_stats.csv of the bench command")
+    c.add_argument("--calibration", required=True, help="calibration.py's summary file")
+    c.add_argument("--M", type=int, default=4608)
+    c.add_argument("--N", type=int, default=3072)
+    c.add_argument("--Kp", type=int, default=3072)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--out", required=True)
+    c.add_argument("--command", default="")
     a = p.parse_args(argv)
+    if a.cmd == "counters":
+        lines = ["# Hardware counters per dispatch (rocprofv3 --pmc, median over dispatches), "
+                 f"W4A4 layer M={a.M} N={a.N} K'={a.Kp}, and the MFMA-only calibration kernel",
+                 f"# command: {a.command}"]
+        lines += counter_summary(a.pmc, a.calib, a.stats, a.calibration, a.M, a.N, a.Kp, a.cus)
+        with open(a.out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return 0
     if a.cmd == "stats":
         for r in kernel_stats(a.csv):
             print(f"{r['calls']:6d} calls  avg {r['avg_us']:9.2f} us  min {r['min_us']:9.2f}  "

@@ -281,3 +281,20 @@ def test_fused_linear_validates_before_launch(lib):
     assert call(wsp=A16 * 16 + 16) == E.CONVROT_ERR_ALIGN
     assert call(nbytes=cr.convrot_w4a4_workspace_bytes(4, 3072, 256) - 1) == E.CONVROT_ERR_WORKSPACE
     assert call(M=0, x=None, y=None) == E.CONVROT_OK
+
+
+def test_calibration_library_exports():
+    """libconvrot_calib.so (built with the layer's library) exports its three calls, and the
+    launcher rejects bad shapes before touching the device."""
+    import ctypes
+    from rotation_w4a4_quantized_convrot_amd import calibration as C
+    if not os.path.exists(C.CALIB_PATH):
+        pytest.skip("libconvrot_calib.so not built")
+    lib = C.load()
+    assert lib.convrot_calib_macs_per_mfma() == 32 * 32 * 32
+    assert lib.convrot_calib_chains() >= 1
+    bad = [(0, 256, 1), (1, 100, 1), (1, 2048, 1), (1, 256, -1)]
+    for grid, block, iters in bad:
+        assert lib.convrot_calib_mfma_i8(grid, block, iters, ctypes.c_void_p(16),
+                                         ctypes.c_void_p(16), None) != 0
+    assert lib.convrot_calib_mfma_i8(1, 256, 1, None, ctypes.c_void_p(16), None) != 0
