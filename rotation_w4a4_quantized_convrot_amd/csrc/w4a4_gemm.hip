@@ -223,9 +223,19 @@ struct Shape {
 };
 
 // 16 bytes at byte `byte` of row `row` (row stride rowB); bytes at or past lim read zero.
+// kTail8: rows of 8 (mod 16) bytes (int4 codes, g = 16 with an odd number of windows), whose
+// last 16-byte chunk holds only 8 bytes of the row: that chunk is read with an 8-byte load
+// and its upper half is zero (a 16-byte load would reach into the next row).
+template <bool kTail8 = false>
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, int row, int byte, int lim,
                                       int rowB) {
   const uint32_t off = byte < lim ? uint32_t(row * rowB + byte) : big::kOob;
+  if constexpr (kTail8) {
+    if (byte + 8 == lim) {
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+      return make_uint4(v.x, v.y, 0u, 0u);
+    }
+  }
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
@@ -247,7 +257,7 @@ struct Frag {
 
 // A step that is not this wave's (valid false) reads zeros without touching memory, so that
 // every wave issues the same loads and the compiler can count them exactly.
-template <int QB, int MB>
+template <int QB, int MB, bool kTail8>
 __device__ __forceinline__ void load_step(Frag<MB>& f, __amdgpu_buffer_rsrc_t rw,
                                           __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rsw,
                                           __amdgpu_buffer_rsrc_t rsx, int step, bool valid,
@@ -258,9 +268,9 @@ __device__ __forceinline__ void load_step(Frag<MB>& f, __amdgpu_buffer_rsrc_t rw
   for (int c = 0; c < 2; ++c) {
     const int q = QB == 4 ? 2 * h + c : 2 * c + h;
     const int byte = step * kStepB + 16 * q;
-    f.w[c] = ld16(rw, r32, byte, lim, rowB);
+    f.w[c] = ld16<kTail8>(rw, r32, byte, lim, rowB);
 #pragma unroll
-    for (int j = 0; j < MB; ++j) f.x[j][c] = ld16(rx, 32 * j + r32, byte, lim, rowB);
+    for (int j = 0; j < MB; ++j) f.x[j][c] = ld16<kTail8>(rx, 32 * j + r32, byte, lim, rowB);
   }
   if constexpr (QB == big::kQbMx) {
     f.sw = ld4(rsw, r32, 4 * step, slim, srow) >> (8 * h);
@@ -316,7 +326,7 @@ __device__ __forceinline__ void mma_step(const Frag<MB>& f, v16i (&acc)[MB]) {
 
 // QB: 4 (packed int4), 8 (int8) or big::kQbMx (MXFP4: packed E2M1 codes with E8M0 block
 // scales in xbs / wbs, fp32 sums; the partial sums of the waves are added in wave order).
-template <bool kDbg, int QB, int MB>
+template <bool kDbg, int QB, int MB, bool kTail8>
 __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
     const float* __restrict__ ws, const uint8_t* __restrict__ xbs,
@@ -387,7 +397,7 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     if (kOrdered || k0 + d < k1)
-      load_step<QB, MB>(f[d], rw, rx, rsw, rsx, k0 + d, k0 + d < k1, rowB, srow, lane);
+      load_step<QB, MB, kTail8>(f[d], rw, rx, rsw, rsx, k0 + d, k0 + d < k1, rowB, srow, lane);
     if constexpr (kOrdered) __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -397,11 +407,11 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
       const int kn = k + d + kDepth;
       if constexpr (kOrdered) {
         mma_step<QB, MB>(f[d], acc);
-        load_step<QB, MB>(f[d], rw, rx, rsw, rsx, kn, kn < k1, rowB, srow, lane);
+        load_step<QB, MB, kTail8>(f[d], rw, rx, rsw, rsx, kn, kn < k1, rowB, srow, lane);
         __builtin_amdgcn_sched_barrier(0);
       } else if (k + d < k1) {
         mma_step<QB, MB>(f[d], acc);
-        if (kn < k1) load_step<QB, MB>(f[d], rw, rx, rsw, rsx, kn, true, rowB, srow, lane);
+        if (kn < k1) load_step<QB, MB, kTail8>(f[d], rw, rx, rsw, rsx, kn, true, rowB, srow, lane);
       }
     }
   }
@@ -701,7 +711,7 @@ hipError_t launch_skinny_lds(const uint8_t* xq, const float* xs, const uint8_t* 
                        xq, xs, wq, ws, bias, int(M), int(N), int(Kp), y, acc_dbg);
 }
 
-template <int QB, int MB>
+template <int QB, int MB, bool kTail8>
 hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* wq,
                             const float* ws, const uint8_t* xbs, const uint8_t* wbs,
                             const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
@@ -709,9 +719,9 @@ hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* w
   const dim3 grid(unsigned((N + skinny::kTN - 1) / skinny::kTN), unsigned((M + 32 * MB - 1) / (32 * MB)));
   const dim3 block(skinny::Shape<MB>::kThreads);
   if (acc_dbg != nullptr)
-    return launch_kernel(skinny::quant_gemm_skinny_kernel<true, QB, MB>, grid, block, 0, stream,
+    return launch_kernel(skinny::quant_gemm_skinny_kernel<true, QB, MB, kTail8>, grid, block, 0, stream,
                          xq, xs, wq, ws, xbs, wbs, bias, int(M), int(N), int(Kp), y, acc_dbg);
-  return launch_kernel(skinny::quant_gemm_skinny_kernel<false, QB, MB>, grid, block, 0, stream, xq,
+  return launch_kernel(skinny::quant_gemm_skinny_kernel<false, QB, MB, kTail8>, grid, block, 0, stream, xq,
                        xs, wq, ws, xbs, wbs, bias, int(M), int(N), int(Kp), y, acc_dbg);
 }
 
@@ -720,6 +730,22 @@ hipError_t launch_skinny_mb(const uint8_t* xq, const float* xs, const uint8_t* w
 constexpr int64_t kSkinnyMaxM4 = 512, kSkinnyMaxM8 = 256, kSkinnyMaxMx = 256;
 // Largest M routed to the LDS-staged int4 skinny kernel.
 constexpr int64_t kSkinnyLdsMaxM = 64;
+// Below this many outputs the 256 x 256 tiles number fewer than 32 and leave most CUs idle;
+// the skinny kernel's 32-column workgroups spread the same work over the chip.  int4:
+// measured faster for every shape tried (M x N x K' = 600x3000x3072: 21.2 against 29.8 us
+// for the 128 x 128 kernel; 1000x1000x3072: 11.8 against 28.6; 4000x500x3072: 22.4 against
+// 29.0; 768x2048x4096: 23.2 against 36.0).
+constexpr int64_t kTiledMinMN = int64_t(1) << 21;
+
+// int8 and MXFP4 codes cost the skinny kernel twice the bytes per MFMA (int8) or fp32 partial
+// sums (MXFP4): below kTiledMinMN it wins only when its grid fits one workgroup per CU
+// (1000x1000x3072: int8 20.8 against 30.8 us, MXFP4 14.9 against 20.8) and loses with
+// two or more (600x3000x3072: int8 37.7 against 31.8, MXFP4 27.0 against 20.9).
+bool skinny_one_wave(int64_t M, int64_t N) {
+  if (M * N >= kTiledMinMN) return false;
+  const int64_t rows = M <= 64 ? 32 : M <= 128 ? 64 : 128;  // activation rows per workgroup
+  return ((N + skinny::kTN - 1) / skinny::kTN) * ((M + rows - 1) / rows) <= device_cus();
+}
 
 // A dispatch counts its work-items in 32-bit fields.  The skinny grid has N / 32 workgroups
 // of up to 1024 threads, so it fits only below about N = 2^27; wider outputs take another
@@ -732,7 +758,7 @@ bool skinny_fits(int64_t M, int64_t N) {
 }
 
 // Activation rows per skinny workgroup: 32, 64 or 128.
-template <int QB>
+template <int QB, bool kTail8 = false>
 hipError_t launch_skinny(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                          const uint16_t* bias, int64_t M, int64_t N, int64_t Kp, uint16_t* y,
                          int32_t* acc_dbg, hipStream_t stream, const uint8_t* xbs = nullptr,
@@ -741,13 +767,13 @@ hipError_t launch_skinny(const uint8_t* xq, const float* xs, const uint8_t* wq, 
   // N = K' = 3072, weights from HBM, M = 64: int4 6.1 against 7.9 us, int8 9.8 against
   // 15.2 us, MXFP4 7.2 against 9.6 us for 64-row workgroups; at M = 96 three row blocks lose).
   if (M <= 64)
-    return launch_skinny_mb<QB, 1>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
+    return launch_skinny_mb<QB, 1, kTail8>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
   // 64-row workgroups up to M = 128: twice the workgroups of the 128-row form and half the
   // K steps per wave (measured at N = K' = 3072, M = 128: int4 7.8 against 11.6 us, int8
   // 14.0 against 22.0 us, MXFP4 9.7 against 14.9 us; from M = 192 the 128-row form wins).
   if (M <= 128)
-    return launch_skinny_mb<QB, 2>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
-  return launch_skinny_mb<QB, 4>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
+    return launch_skinny_mb<QB, 2, kTail8>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
+  return launch_skinny_mb<QB, 4, kTail8>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, y, acc_dbg, stream);
 }
 
 template <int QB>
@@ -782,12 +808,16 @@ hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
   // skinny form).
   if (rows16 && M <= kSkinnyLdsMaxM && skinny_fits(M, N))
     return launch_skinny_lds(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-  if (rows16 && M <= kSkinnyMaxM4 && skinny_fits(M, N))
-    return launch_skinny<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
-  // The large tile needs 16-byte packed rows and enough work to fill the chip (or an output
-  // too wide for the skinny grid).
-  if (rows16 && ((M * N >= (int64_t(1) << 21) && M >= big::kBM / 2) || M <= kSkinnyMaxM4))
-    return launch_big<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+  // Rows of K'/2 = 8 (mod 16) bytes (g = 16 with an odd number of windows) take the skinny
+  // kernel's 8-byte tail loads.
+  if ((M <= kSkinnyMaxM4 || M * N < kTiledMinMN) && skinny_fits(M, N))
+    return rows16 ? launch_skinny<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream)
+                  : launch_skinny<4, true>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+  if (rows16) return launch_big<4>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
+  // Larger outputs with 8 (mod 16)-byte rows: the buffer-to-LDS transfers of the tiled kernel
+  // move 16 bytes per lane, so these take the 128 x 128 kernel, which reads them with 8-byte
+  // loads (measured 79.6 us at M x N x K' = 4608 x 3072 x 3088, against 39.3 us for the
+  // tiled kernel at K' = 3072).
   const dim3 grid(unsigned(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN)));
   const dim3 block(256);
   if (vec_bytes == 16)
@@ -802,7 +832,7 @@ hipError_t launch_w8a8_gemm(const uint8_t* xq, const float* xs, const uint8_t* w
                             int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   // int8 operands double the skinny kernel's bytes per MFMA: it wins up to M = 256.
-  if (M <= kSkinnyMaxM8 && skinny_fits(M, N))
+  if ((M <= kSkinnyMaxM8 || skinny_one_wave(M, N)) && skinny_fits(M, N))
     return launch_skinny<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
   return launch_big<8>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, stream);
 }
@@ -812,7 +842,7 @@ hipError_t launch_mxfp4_gemm(const uint8_t* xq, const uint8_t* xbs, const uint8_
                              int64_t Kp, uint16_t* y, float* acc_dbg, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   int32_t* dbg = reinterpret_cast<int32_t*>(acc_dbg);
-  if (M <= kSkinnyMaxMx && skinny_fits(M, N))
+  if ((M <= kSkinnyMaxMx || skinny_one_wave(M, N)) && skinny_fits(M, N))
     return launch_skinny<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream,
                                      xbs, wbs);
   return launch_big<big::kQbMx>(xq, nullptr, wq, nullptr, bias, M, N, Kp, y, dbg, stream, xbs,

@@ -172,8 +172,10 @@ def test_empty_inputs(cr):
 
 GEMM_CASES = [
     # M, N, Kp, bias
-    # K'/2 not a multiple of 16: the 128 x 128 kernel
-    (1, 1, 16, False), (17, 5, 48, True), (700, 300, 1040, True),
+    # K'/2 = 8 (mod 16), M <= 512: the skinny kernel with 8-byte row tails (32-, 64- and
+    # 128-row workgroups, one and several K steps)
+    (1, 1, 16, False), (17, 5, 48, True), (700, 300, 1040, True), (64, 700, 3088, True),
+    (100, 33, 1552, False), (200, 300, 3088, False),
     # M <= 512: the skinny kernel (32, 64 and 128-row workgroups, ragged M, N and K)
     (1, 40, 128, True), (128, 128, 128, False), (200, 136, 1024, True), (129, 130, 256, True),
     (300, 257, 3072, False), (64, 256, 3328, True), (33, 96, 12288, False),
@@ -181,6 +183,11 @@ GEMM_CASES = [
     # M <= 64 (LDS-staged skinny kernel): one partial round with ragged N, exactly two
     # rounds, three rounds (an odd count, the last one half full), eight rounds
     (63, 2, 1056, True), (32, 33, 4096, False), (64, 3000, 5120, True), (40, 1000, 16384, False),
+    # M > 512 but M N < 2^21: the skinny kernel (128-row workgroups), ragged M and N
+    (1000, 1000, 512, True), (4000, 500, 256, False), (600, 3000, 320, True), (513, 4087, 96, False),
+    # K'/2 = 8 (mod 16): mid size (M N < 2^21, skinny with row tails) and large (M N >= 2^21,
+    # the 128 x 128 kernel)
+    (1000, 1000, 528, True), (2100, 1100, 208, False), (4608, 3072, 3088, True),
     # large-tile kernel (M N >= 2^21): ragged M and N, several tiles, K tails
     (600, 3500, 512, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
     (4607, 3071, 128, False), (1130, 1990, 576, True), (4000, 4090, 320, True),

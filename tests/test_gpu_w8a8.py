@@ -121,8 +121,10 @@ GEMM_CASES = [
     # M <= 256: the skinny kernel
     (1, 1, 16, False), (64, 64, 64, True), (100, 200, 512, True), (129, 257, 1040, False),
     (256, 3000, 3072, True), (16, 3072, 12288, False), (48, 300, 1040, True),
-    # the tiled kernel
-    (300, 500, 320, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
+    # M > 256 with M N < 2^21 and at most one workgroup per CU: the skinny kernel
+    (300, 500, 320, True), (1000, 1000, 512, False),
+    # the tiled kernel (M N < 2^21 but more skinny workgroups than CUs; larger outputs)
+    (600, 3000, 320, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
 ]
 
 
