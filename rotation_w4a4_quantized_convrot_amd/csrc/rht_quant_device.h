@@ -192,21 +192,24 @@ __device__ __forceinline__ void load_raw(__amdgpu_buffer_rsrc_t rs, uint32_t off
   }
 }
 
-// Zeroes the elements of a chunk starting at column col that lie at or past column K.
+// Zeroes the elements of a chunk of which only the first `rem` (K minus the chunk's first
+// column) lie before column K.  Comparing rem with constants keeps the per-element column
+// numbers out of registers: computed from the loop-invariant columns, they would be hoisted
+// and held live through the whole loop for this rarely taken path.
 template <typename TIn>
-__device__ __forceinline__ void mask_tail(RawChunk<TIn>& c, int col, int K) {
+__device__ __forceinline__ void mask_tail(RawChunk<TIn>& c, int rem) {
   if constexpr (sizeof(TIn) == 2) {
     uint32_t w[4] = {c.w.x, c.w.y, c.w.z, c.w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t keep = (col + 2 * i < K ? 0xFFFFu : 0u) | (col + 2 * i + 1 < K ? 0xFFFF0000u : 0u);
+      const uint32_t keep = (2 * i < rem ? 0xFFFFu : 0u) | (2 * i + 1 < rem ? 0xFFFF0000u : 0u);
       w[i] &= keep;
     }
     c.w = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     uint32_t w[8] = {c.w0.x, c.w0.y, c.w0.z, c.w0.w, c.w1.x, c.w1.y, c.w1.z, c.w1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = col + i < K ? w[i] : 0u;
+    for (int i = 0; i < 8; ++i) w[i] = i < rem ? w[i] : 0u;
     c.w0 = make_uint4(w[0], w[1], w[2], w[3]);
     c.w1 = make_uint4(w[4], w[5], w[6], w[7]);
   }
@@ -432,7 +435,7 @@ __device__ __forceinline__ void rht_quant_body(const TIn* __restrict__ x, int M,
       int Kc = K;
       asm volatile("" : "+s"(Kc));
 #pragma unroll
-      for (int r = 0; r < C; ++r) mask_tail<TIn>(raw[r], j * G + 8 * chunk_of<G>(lu, r), Kc);
+      for (int r = 0; r < C; ++r) mask_tail<TIn>(raw[r], Kc - (j * G + 8 * chunk_of<G>(lu, r)));
     }
     if constexpr (!kMx) {  // raw window data, in position order, for the exact recomputation
       uint8_t* wb = rawwin + (wave * U + unit) * (G * ES);
