@@ -227,7 +227,10 @@ __device__ __forceinline__ void mma_unp(const Unp& u, v16i (&acc)[kGN][kGM]) {
 //      nearest even by v_cvt_pk_bf16_f32) and writes them into the wave's own 32 x 128
 //      staging rows; the wave then reads the rows back and stores 16 contiguous bytes per
 //      lane, four whole 256-byte output rows per instruction.
-template <bool kDbg, int QB>
+// kFold (int4): the sums are 256 t; fp32(256 t) = 256 fp32(t) exactly, so fp32(256 t) times
+// sxm / 256 rounds exactly as fp32(t) times sxm whenever sxm / 256 is exact (sxm zero or at
+// least 2^-118).  sxm then arrives already divided by 256 and the shift is skipped.
+template <bool kDbg, int QB, bool kFold>
 __device__ __forceinline__ void epi_block(const v16i (&acc)[kGN][kGM], int j, float sxm,
                                           const float* fw, const float* fb, uint8_t* stage,
                                           int M, int N, long mrow, long n0, int wn, int lane,
@@ -253,7 +256,8 @@ __device__ __forceinline__ void epi_block(const v16i (&acc)[kGN][kGM], int j, fl
         } else {
           // int4 operands enter the MFMA as 16 q: every product is a multiple of 256
           t[r] = QB == 4 ? acc[i][j][4 * g + r] >> 8 : acc[i][j][4 * g + r];
-          z[r] = __fadd_rn(__fmul_rn(__fmul_rn((float)t[r], sxm), wv[r]), bv[r]);
+          const float a = kFold ? (float)acc[i][j][4 * g + r] : (float)t[r];
+          z[r] = __fadd_rn(__fmul_rn(__fmul_rn(a, sxm), wv[r]), bv[r]);
         }
       }
       if (kDbg && mrow + r32 < M) {  // raw integer sums, for verification only
@@ -284,16 +288,36 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
   // Each wave's 32 x 128 staging rows: three per stage buffer.
   uint8_t* stage = (wave < 3 ? st0 : wave < 6 ? st1 : st2) + (wave % 3) * (32 * kPitch);
   const bool vec16 = (N & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+  // 32 output rows fit a buffer resource with 32-bit offsets (all but outputs of more than
+  // 2^25 columns): its range check drops the rows past M, with no per-store address
+  // arithmetic in 64 bits.
+  const bool rows32 = long(N) * 64 < 0x7FFFFFF0L;
 #pragma unroll
   for (int j = 0; j < kGM; ++j) {
     const long mrow = m0 + wm * kTM + 32 * j;  // first output row of this block
     const float sxm = fx[wm * kTM + 32 * j + r32];
-    epi_block<kDbg, QB>(acc, j, sxm, fw, fb, stage, M, N, mrow, n0, wn, lane, acc_dbg);
+    if (QB == 4 && __builtin_amdgcn_ballot_w64(sxm != 0.0f && fabsf(sxm) < 0x1p-118f) == 0)
+      epi_block<kDbg, QB, QB == 4>(acc, j, sxm * 0x1p-8f, fw, fb, stage, M, N, mrow, n0, wn,
+                                   lane, acc_dbg);
+    else
+      epi_block<kDbg, QB, false>(acc, j, sxm, fw, fb, stage, M, N, mrow, n0, wn, lane, acc_dbg);
     // Same wave, in-order LDS: the rows written above are complete for the reads below.
     __builtin_amdgcn_wave_barrier();
     const int c16 = lane & 15;
     const long n = n0 + wn * kTN + 8 * c16;
-    if (vec16) {
+    if (vec16 && rows32) {
+      const __amdgpu_buffer_rsrc_t ry = rsrc(y + mrow * (long)N, min(long(M) - mrow, 32L) * N * 2);
+      if (n < N) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int row = 4 * t + (lane >> 4);
+          const uint4 v = *reinterpret_cast<const uint4*>(stage + row * kPitch + 16 * c16);
+          // streaming store (nt): the output is not re-read here
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ry,
+                                                 uint32_t((row * N + n) * 2), 0, 2);
+        }
+      }
+    } else if (vec16) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int row = 4 * t + (lane >> 4);
