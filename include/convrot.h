@@ -284,6 +284,29 @@ CONVROT_API int convrot_w4a4_linear_fused(const void* x, int32_t x_dtype, int64_
                                           size_t ws_bytes, uint32_t* status, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Analysis helpers, not on the layer's path: the int4 quantization rule of a3-a4 applied to
+ * rows that are already transformed (no rotation), and the inverse mapping of packed codes.
+ * The outlier-suppression tool uses them to quantize its comparison transforms (none,
+ * Sylvester-type Hadamard) by the same rule as the layer ([HSWQ] "Hadamard Orthogonal
+ * Rotation": per-row scale = max|row| / q_max, code = round(value / scale), here with q_max = 7,
+ * round half to even, codes clamped to [-8, 7]; [KITCHEN]: two codes per byte, column 2j in
+ * the low nibble).  Device pointers, owned by the caller; calls enqueue on `stream`.
+ *
+ * convrot_quant_rows_int4: y fp32 [M][ldy] (ldy >= K elements; y 4-byte aligned) ->
+ *   q [M][(K + 1) / 2] packed codes (an odd K leaves a zero code in each row's last high
+ *   nibble) and s [M] fp32 (4-byte aligned): s = fp32(max_k |y[m][k]| / 7) by IEEE division,
+ *   code = clamp(rne(fp32(y / s)), -8, 7), all codes 0 where s == 0.  Rows holding NaN give
+ *   unspecified codes.  Errors: NULL, SHAPE (M < 0, M >= 2^31, K < 1, ldy < K), ALIGN, HIP. */
+CONVROT_API int convrot_quant_rows_int4(const float* y, int64_t M, int64_t K, int64_t ldy,
+                                        uint8_t* q, float* s, void* stream);
+
+/* convrot_dequant_int4: q [M][(K + 1) / 2] packed codes as above, s [M] fp32 (4-byte aligned)
+ *   -> out fp64 [M][K] (8-byte aligned), out = code * s, exact.  Errors: NULL, SHAPE (M < 0,
+ *   K < 1, M * K >= 2^40), ALIGN, HIP. */
+CONVROT_API int convrot_dequant_int4(const uint8_t* q, const float* s, int64_t M, int64_t K,
+                                     double* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the ConvLinear4bit forward pass of
  * convrot_w4a4_linear without a workspace argument.  The packed activation codes and row

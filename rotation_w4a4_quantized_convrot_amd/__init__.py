@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     convrot_rotate_quant_act_mxfp4, convrot_quant_weight_mxfp4, convrot_mxfp4_gemm,
     convrot_mxfp4_workspace_bytes, convrot_mxfp4_linear, mx_scale_stride,
     convrot_w4a4_linear_noalloc, CONVROT_NOALLOC_SCRATCH_BYTES, convrot_w4a4_linear_fused,
+    convrot_quant_rows_int4, convrot_dequant_int4,
 )
 from .linear import ConvLinear4bit, ConvLinear8bit, ConvLinearFP4  # noqa: F401
 
@@ -24,5 +25,5 @@ __all__ = [
     "convrot_w8a8_gemm", "convrot_w8a8_workspace_bytes", "convrot_w8a8_linear",
     "convrot_rotate_quant_act_mxfp4", "convrot_quant_weight_mxfp4", "convrot_mxfp4_gemm",
     "convrot_mxfp4_workspace_bytes", "convrot_mxfp4_linear", "convrot_w4a4_linear_noalloc",
-    "convrot_w4a4_linear_fused",
+    "convrot_w4a4_linear_fused", "convrot_quant_rows_int4", "convrot_dequant_int4",
 ]

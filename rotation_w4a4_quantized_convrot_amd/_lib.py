@@ -62,6 +62,8 @@ SIGNATURES = {
                                              _vp, _vp]),
     "convrot_w4a4_linear_fused": (_c_int, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp,
                                            _vp, ctypes.c_size_t, _vp, _vp]),
+    "convrot_quant_rows_int4": (_c_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "convrot_dequant_int4": (_c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -525,3 +527,49 @@ def convrot_mxfp4_linear(x: torch.Tensor, g: int, wq: torch.Tensor, wbs: torch.T
     """The MXFP4 ConvRot forward pass: x [M, K] contiguous -> y bf16 [M, N]."""
     return _linear(load_library().convrot_mxfp4_linear, convrot_mxfp4_workspace_bytes, x, g, wq,
                    wbs, bias, y, workspace, _half, True)
+
+
+# ----------------------------------------------------------------- analysis helpers
+def convrot_quant_rows_int4(y: torch.Tensor, q: Optional[torch.Tensor] = None,
+                            s: Optional[torch.Tensor] = None):
+    """Per-row int4 codes of already-transformed rows (no rotation): y fp32 [M, K] (rows may be
+    strided) -> (q uint8 [M, ceil(K/2)], s fp32 [M]), the layer's quantization rule."""
+    _is_tensor(y, "y")
+    if y.dim() != 2:
+        raise ValueError(f"y must be 2-D, got {y.dim()} dimensions")
+    if y.dtype != torch.float32:
+        raise TypeError(f"y must be torch.float32, got {y.dtype}")
+    if y.stride(1) != 1 and y.shape[1] > 1:
+        raise ValueError("y must be 2-D with unit column stride")
+    M, K = int(y.shape[0]), int(y.shape[1])
+    cols = (K + 1) // 2
+    _mat(q, "q", M, cols, _CODE_BYTES)
+    _vec(s, "s", M, torch.float32)
+    dev = _require_device(y, q, s)
+    if q is None:
+        q = torch.empty((M, cols), dtype=torch.uint8, device=dev)
+    if s is None:
+        s = torch.empty((M,), dtype=torch.float32, device=dev)
+    _check(load_library().convrot_quant_rows_int4(_ptr(y), M, K, y.stride(0), _ptr(q), _ptr(s),
+                                                  _stream(dev)))
+    return q, s
+
+
+def convrot_dequant_int4(q: torch.Tensor, s: torch.Tensor, K: int,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed int4 codes q [M, ceil(K/2)] and row scales s [M] -> fp64 [M, K], code * scale."""
+    M, cols = _codes_2d(q, "q")
+    if q.dtype not in _CODE_BYTES:
+        raise TypeError(f"q must be torch.uint8 or torch.int8, got {q.dtype}")
+    if cols != (K + 1) // 2:
+        raise ValueError(f"q must have {(K + 1) // 2} bytes per row for K = {K}, got {cols}")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _vec(s, "s", M, torch.float32)
+    _mat(out, "out", M, K, (torch.float64,))
+    dev = _require_device(q, s, out)
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float64, device=dev)
+    _check(load_library().convrot_dequant_int4(_ptr(q), _ptr(s), M, K, _ptr(out), _stream(dev)))
+    return out
+

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libconvrot.so")
-SOURCES = ("api.hip", "rht_quant.hip", "w4a4_gemm.hip", "fused.hip")
+SOURCES = ("api.hip", "rht_quant.hip", "w4a4_gemm.hip", "fused.hip", "rowquant.hip")
 CALIB_PATH = os.path.join(PKG, "libconvrot_calib.so")
 CALIB_SOURCES = ("calib.hip",)
 ARCH = "gfx950"

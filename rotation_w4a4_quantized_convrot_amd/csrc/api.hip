@@ -446,3 +446,25 @@ extern "C" int convrot_w4a4_linear_noalloc(const void* x, int32_t x_dtype, int64
   return convrot_w4a4_linear(x, x_dtype, M, K, g, wq, ws, N, bias, y, work,
                              CONVROT_NOALLOC_SCRATCH_BYTES, stream);
 }
+
+int convrot_quant_rows_int4(const float* y, int64_t M, int64_t K, int64_t ldy, uint8_t* q,
+                            float* s, void* stream) {
+  if (M < 0 || M >= (int64_t(1) << 31) || K < 1 || ldy < K || K >= (int64_t(1) << 31))
+    return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (y == nullptr || q == nullptr || s == nullptr) return CONVROT_ERR_NULL;
+  if (!aligned(y, 4) || !aligned(s, 4)) return CONVROT_ERR_ALIGN;
+  return status_of(convrot::launch_quant_rows_int4(y, M, K, ldy, q, s,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int convrot_dequant_int4(const uint8_t* q, const float* s, int64_t M, int64_t K, double* out,
+                         void* stream) {
+  if (M < 0 || K < 1 || K >= (int64_t(1) << 31) || (M > 0 && M > (int64_t(1) << 40) / K))
+    return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (q == nullptr || s == nullptr || out == nullptr) return CONVROT_ERR_NULL;
+  if (!aligned(s, 4) || !aligned(out, 8)) return CONVROT_ERR_ALIGN;
+  return status_of(convrot::launch_dequant_int4(q, s, M, K, out, static_cast<hipStream_t>(stream)));
+}
+

@@ -64,4 +64,10 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
   }(static_cast<KArgs>(args)...);
 }
 
+// Analysis helpers (rowquant.hip): per-row int4 quantization without rotation, dequantization.
+hipError_t launch_quant_rows_int4(const float* y, int64_t M, int64_t K, int64_t ldy, uint8_t* q,
+                                  float* s, hipStream_t stream);
+hipError_t launch_dequant_int4(const uint8_t* q, const float* s, int64_t M, int64_t K,
+                               double* out, hipStream_t stream);
+
 }  // namespace convrot

@@ -18,8 +18,9 @@ What runs where:
     ConvLinear4bit output: the HIP kernels, through the C ABI;
   * the comparison transforms the kernels do not implement (none, group-wise Sylvester,
     global Sylvester over the row zero-padded to a power of two): torch on the same device,
-    with a fast Walsh-Hadamard transform; their int4 codes follow the same rule (scale =
-    absmax / 7, round half to even, clamp to [-8, 7]).
+    with a fast Walsh-Hadamard transform.  Their int4 codes and scales come from the library's
+    convrot_quant_rows_int4 (the layer's quantization rule without the rotation), and every
+    dequantization from convrot_dequant_int4: no quantization arithmetic is repeated here.
   * every W4A4 error is evaluated the same way, as the float64 product of the dequantized
     codes; the kernels' own bf16 output error is reported beside it for the regular transform.
 
@@ -89,14 +90,12 @@ def sylvester_global(x: torch.Tensor) -> torch.Tensor:
     return fwht(_pad_cols(x.double(), n)) / math.sqrt(n)
 
 
-def int4_codes(y: torch.Tensor):
-    """Symmetric per-row int4: scale = fp32(absmax / 7), codes = clamp(rne(y / scale))."""
-    yf = y.float()
-    s = (yf.abs().amax(dim=1) / 7.0).float()
-    safe = torch.where(s > 0, s, torch.ones_like(s))
-    q = torch.round(yf / safe[:, None]).clamp(-8, 7)
-    q = torch.where(s[:, None] > 0, q, torch.zeros_like(q))
-    return q.double(), s.double()
+def int4_dequantized(y: torch.Tensor) -> torch.Tensor:
+    """Rows of y (a comparison transform's output, rounded to fp32) quantized to int4 per row
+    and dequantized, by the library (fp64 result)."""
+    from . import convrot_dequant_int4, convrot_quant_rows_int4
+    q, s = convrot_quant_rows_int4(y.float().contiguous())
+    return convrot_dequant_int4(q, s, y.shape[1])
 
 
 def rel_frobenius(a: torch.Tensor, ref: torch.Tensor) -> float:
@@ -104,19 +103,9 @@ def rel_frobenius(a: torch.Tensor, ref: torch.Tensor) -> float:
     return float(torch.linalg.norm(a.double() - ref.double()) / den) if den > 0 else 0.0
 
 
-def unpack_int4(xq: torch.Tensor) -> torch.Tensor:
-    """Packed int4 codes [rows, K'/2] (code 2j in the low nibble) -> int codes [rows, K']."""
-    b = xq.to(torch.int32)
-    lo, hi = b & 0xF, (b >> 4) & 0xF
-    lo = torch.where(lo >= 8, lo - 16, lo)
-    hi = torch.where(hi >= 8, hi - 16, hi)
-    return torch.stack((lo, hi), dim=2).reshape(xq.shape[0], 2 * xq.shape[1])
-
-
-def _row(name: str, g: Optional[int], disc: Optional[float], y: torch.Tensor, q: torch.Tensor,
-         s: torch.Tensor, w_deq: Optional[torch.Tensor], ref: Optional[torch.Tensor],
+def _row(name: str, g: Optional[int], disc: Optional[float], y: torch.Tensor,
+         deq: torch.Tensor, w_deq: Optional[torch.Tensor], ref: Optional[torch.Tensor],
          bias: Optional[torch.Tensor]) -> dict:
-    deq = q * s[:, None]
     r = {"transform": name, "g": g, "column_discrepancy": disc,
          "max_abs": float(y.abs().max()), "act_int4_rel_err": rel_frobenius(deq, y)}
     if w_deq is not None:
@@ -131,7 +120,8 @@ def analyze(x: torch.Tensor, groups: Sequence[int] = GROUPS, w: Optional[torch.T
             bias: Optional[torch.Tensor] = None) -> Dict[str, object]:
     """Every transform's statistics for X (device tensor [M, K], bf16 or fp32), and with a
     weight W [N, K] (same device) the W4A4 errors against float64 X W^T (+ bias)."""
-    from . import convrot_quant_weight, convrot_rotate_quant_act, convrot_w4a4_linear
+    from . import (convrot_dequant_int4, convrot_quant_weight, convrot_rotate_quant_act,
+                   convrot_w4a4_linear)
     rows = []
     ref = None
     if w is not None:
@@ -139,12 +129,9 @@ def analyze(x: torch.Tensor, groups: Sequence[int] = GROUPS, w: Optional[torch.T
         if bias is not None:
             ref = ref + bias.double()[None, :]
     # no rotation
-    q, s = int4_codes(x.double())
-    wd = None
-    if w is not None:
-        qw, sw = int4_codes(w.double())
-        wd = qw * sw[:, None]
-    rows.append(_row("none", None, None, x.double(), q, s, wd, ref, bias))
+    wd = None if w is None else int4_dequantized(w.double())
+    rows.append(_row("none", None, None, x.double(), int4_dequantized(x.double()), wd, ref,
+                     bias))
     for g in groups:
         # regular, group-wise: the HIP kernels
         xq, xs, xr = convrot_rotate_quant_act(x, g, want_rotated=True)
@@ -152,31 +139,23 @@ def analyze(x: torch.Tensor, groups: Sequence[int] = GROUPS, w: Optional[torch.T
         wd = None
         if w is not None:
             wq, ws = convrot_quant_weight(w, g)
-            wd = unpack_int4(wq).double() * ws.double()[:, None]
-        r = _row("regular", g, column_discrepancy(h), xr.double(), unpack_int4(xq).double(),
-                 xs.double(), wd, ref, bias)
+            wd = convrot_dequant_int4(wq, ws, 2 * wq.shape[1])
+        r = _row("regular", g, column_discrepancy(h), xr.double(),
+                 convrot_dequant_int4(xq, xs, 2 * xq.shape[1]), wd, ref, bias)
         if w is not None:
             r["w4a4_rel_err_kernel_bf16"] = rel_frobenius(convrot_w4a4_linear(x, g, wq, ws, bias),
                                                           ref)
         rows.append(r)
         # Sylvester, group-wise
         y = sylvester_groups(x, g)
-        q, s = int4_codes(y)
-        wd = None
-        if w is not None:
-            qw, sw = int4_codes(sylvester_groups(w, g))
-            wd = qw * sw[:, None]
-        rows.append(_row("sylvester", g, column_discrepancy(sylvester_pm1(g)), y, q, s, wd, ref,
-                         bias))
+        wd = None if w is None else int4_dequantized(sylvester_groups(w, g))
+        rows.append(_row("sylvester", g, column_discrepancy(sylvester_pm1(g)), y,
+                         int4_dequantized(y), wd, ref, bias))
     # Sylvester, global (one transform over the whole zero-padded row)
     y = sylvester_global(x)
     n = y.shape[1]
-    q, s = int4_codes(y)
-    wd = None
-    if w is not None:
-        qw, sw = int4_codes(sylvester_global(w))
-        wd = qw * sw[:, None]
-    rows.append(_row("sylvester_global", n, float(n), y, q, s, wd, ref, bias))
+    wd = None if w is None else int4_dequantized(sylvester_global(w))
+    rows.append(_row("sylvester_global", n, float(n), y, int4_dequantized(y), wd, ref, bias))
     return {"M": int(x.shape[0]), "K": int(x.shape[1]), "transforms": rows}
 
 

@@ -298,3 +298,20 @@ def test_calibration_library_exports():
         assert lib.convrot_calib_mfma_i8(grid, block, iters, ctypes.c_void_p(16),
                                          ctypes.c_void_p(16), None) != 0
     assert lib.convrot_calib_mfma_i8(1, 256, 1, None, ctypes.c_void_p(16), None) != 0
+
+
+def test_row_quant_helpers_validate(lib):
+    """Shape, NULL and alignment errors come back before anything is enqueued."""
+    import ctypes
+    p = ctypes.c_void_p(64)
+    assert lib.convrot_quant_rows_int4(p, -1, 8, 8, p, p, None) == _lib.CONVROT_ERR_SHAPE
+    assert lib.convrot_quant_rows_int4(p, 4, 8, 7, p, p, None) == _lib.CONVROT_ERR_SHAPE
+    assert lib.convrot_quant_rows_int4(p, 4, 0, 8, p, p, None) == _lib.CONVROT_ERR_SHAPE
+    assert lib.convrot_quant_rows_int4(None, 4, 8, 8, p, p, None) == _lib.CONVROT_ERR_NULL
+    assert lib.convrot_quant_rows_int4(ctypes.c_void_p(66), 4, 8, 8, p, p, None) == \
+        _lib.CONVROT_ERR_ALIGN
+    assert lib.convrot_quant_rows_int4(p, 0, 8, 8, None, None, None) == _lib.CONVROT_OK
+    assert lib.convrot_dequant_int4(p, p, 4, 0, p, None) == _lib.CONVROT_ERR_SHAPE
+    assert lib.convrot_dequant_int4(p, p, 1 << 40, 2, p, None) == _lib.CONVROT_ERR_SHAPE
+    assert lib.convrot_dequant_int4(p, None, 4, 8, p, None) == _lib.CONVROT_ERR_NULL
+    assert lib.convrot_dequant_int4(p, p, 4, 8, ctypes.c_void_p(68), None) == _lib.CONVROT_ERR_ALIGN

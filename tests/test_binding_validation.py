@@ -169,3 +169,16 @@ def test_from_linear_checks_bias_length():
         cr.ConvLinear4bit.from_linear(z((N, K), bf16), z((N + 1,), bf16), group_size=16)
     with pytest.raises(ValueError, match="2-D"):
         cr.ConvLinear4bit.from_linear(z((N * K,), bf16), None, group_size=16)
+
+
+def test_row_quant_helpers_checked():
+    y = z((M, K), f32)
+    _reaches_device_check(cr.convrot_quant_rows_int4, y, z((M, (K + 1) // 2), u8), z((M,), f32))
+    _raises(cr.convrot_quant_rows_int4, z((M, K), bf16), match="float32")
+    _raises(cr.convrot_quant_rows_int4, y, z((M, K // 2 + 1), u8), match="q")
+    _raises(cr.convrot_quant_rows_int4, y, None, z((M + 1,), f32), match="s")
+    _reaches_device_check(cr.convrot_dequant_int4, z((M, 50), u8), z((M,), f32), 100)
+    _raises(cr.convrot_dequant_int4, z((M, 50), u8), z((M,), f32), 102, match="bytes per row")
+    _raises(cr.convrot_dequant_int4, z((M, 50), f32), z((M,), f32), 100, match="q")
+    _raises(cr.convrot_dequant_int4, z((M, 50), u8), z((M,), f32), 100, z((M, 100), f32),
+            match="out")

@@ -51,17 +51,3 @@ def test_sylvester_concentrates_a_constant_row():
     assert float(y.abs().max()) == pytest.approx(c * np.sqrt(g))
     assert int((y.abs() > 1e-9).sum()) == 1
     assert np.allclose(O.rotate_groups(x.numpy(), g), c)
-
-
-def test_int4_rule_matches_oracle():
-    rng = np.random.default_rng(9)
-    y = (rng.standard_normal((40, 96)) * np.exp2(rng.integers(-4, 4, size=(40, 1)))).astype(np.float32)
-    y[3] = 0.0
-    q, s = T.int4_codes(torch.from_numpy(y).double())
-    assert np.array_equal(s.float().numpy().view(np.uint32), O.row_scales(y).view(np.uint32))
-    assert np.array_equal(q.numpy().astype(np.int8), O.quantize(y, O.row_scales(y)))
-
-
-def test_unpack_matches_oracle():
-    b = np.random.default_rng(2).integers(0, 256, size=(7, 24), dtype=np.int64).astype(np.uint8)
-    assert np.array_equal(T.unpack_int4(torch.from_numpy(b)).numpy(), O.unpack_int4(b))
