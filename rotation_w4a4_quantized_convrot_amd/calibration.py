@@ -1,11 +1,15 @@
-"""Matrix-core rate and shader clock of the GPU, measured with libconvrot_calib.so.
+"""Matrix-core rates and shader clock of the GPU, measured with libconvrot_calib.so.
 
 ``python -m rotation_w4a4_quantized_convrot_amd.calibration [--out FILE]`` runs the
-MFMA-only kernel (v_mfma_i32_32x32x32_i8 in four independent chains per wave, nothing else in
-flight) at one, two and four waves per SIMD, one workgroup per compute unit, each launch about
-0.15 s long, and reports for each:
-  * the int8 rate in POP/s (two ops per multiply-accumulate) and its fraction of MI355X's
-    published dense int8 peak, 5.0 POP/s;
+MFMA-only kernels (one instruction in four independent chains per wave, nothing else in
+flight), one workgroup per compute unit, each launch about 0.15 s long:
+v_mfma_i32_32x32x32_i8 (the int4 and int8 GEMMs) at one, two and four waves per SIMD, and the
+E2M1 forms of v_mfma_scale_f32_32x32x64_f8f6f4 (the MXFP4 GEMM) and
+v_mfma_scale_f32_16x16x128_f8f6f4 at two, and the int8 instruction again at two with operands
+that change every instruction (random full-range int8, and random 16 q as the int4 GEMM feeds
+it).  For each it reports:
+  * the rate in POP/s (two ops per multiply-accumulate) and its fraction of MI355X's
+    published dense peak for that type (int8 5.0 POP/s, fp4 10.1 PFLOP/s);
   * the shader clock while the loop ran: for every workgroup, shader clock cycles
     (s_memtime) over the 100 MHz real-time counter (s_memrealtime) between the same two
     points; median, minimum and maximum over the workgroups.
@@ -25,6 +29,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CALIB_PATH = os.path.join(PKG, "libconvrot_calib.so")
 PEAK_INT8_POPS = 5.0e15
 PEAK_CLOCK_HZ = 2.4e9
+# instruction kind -> (name, published dense peak of its type in ops/s)
+KINDS = {0: ("i8_32x32x32", 5.0e15), 1: ("fp4_32x32x64_scaled", 10.1e15),
+         2: ("fp4_16x16x128_scaled", 10.1e15), 3: ("i8_32x32x32_random_int8", 5.0e15),
+         4: ("i8_32x32x32_random_16q", 5.0e15)}
 REALTIME_HZ = 100e6
 
 
@@ -33,15 +41,16 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(f"{CALIB_PATH} is not built (python -m "
                            "rotation_w4a4_quantized_convrot_amd.build)")
     lib = ctypes.CDLL(CALIB_PATH)
-    lib.convrot_calib_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    lib.convrot_calib_mfma_i8.restype = ctypes.c_int
-    lib.convrot_calib_macs_per_mfma.restype = ctypes.c_int64
+    lib.convrot_calib_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.convrot_calib_mfma.restype = ctypes.c_int
+    lib.convrot_calib_ops_per_inst.argtypes = [ctypes.c_int]
+    lib.convrot_calib_ops_per_inst.restype = ctypes.c_int64
     lib.convrot_calib_chains.restype = ctypes.c_int
     return lib
 
 
-def run(lib, grid: int, block: int, iters: int) -> dict:
+def run(lib, grid: int, block: int, iters: int, kind: int = 0) -> dict:
     """One timed launch; returns its POP/s and the per-workgroup clocks in Hz."""
     import torch
     sink = torch.empty(grid * block, dtype=torch.int32, device="cuda")
@@ -49,15 +58,15 @@ def run(lib, grid: int, block: int, iters: int) -> dict:
     stream = torch.cuda.current_stream()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
-    rc = lib.convrot_calib_mfma_i8(grid, block, iters, ctypes.c_void_p(sink.data_ptr()),
-                                   ctypes.c_void_p(clocks.data_ptr()),
-                                   ctypes.c_void_p(stream.cuda_stream))
+    rc = lib.convrot_calib_mfma(kind, grid, block, iters, ctypes.c_void_p(sink.data_ptr()),
+                                ctypes.c_void_p(clocks.data_ptr()),
+                                ctypes.c_void_p(stream.cuda_stream))
     if rc != 0:
-        raise RuntimeError(f"convrot_calib_mfma_i8 failed: hipError {rc}")
+        raise RuntimeError(f"convrot_calib_mfma failed: hipError {rc}")
     b.record(stream)
     b.synchronize()
     sec = a.elapsed_time(b) / 1e3
-    ops = 2 * lib.convrot_calib_macs_per_mfma() * lib.convrot_calib_chains() * iters * grid * (block // 64)
+    ops = lib.convrot_calib_ops_per_inst(kind) * lib.convrot_calib_chains() * iters * grid * (block // 64)
     c = clocks.view(grid, 4).cpu().tolist()
     hz = [(t1 - t0) / ((r1 - r0) / REALTIME_HZ) for t0, t1, r0, r1 in c if r1 > r0]
     return {"sec": sec, "pops": ops / sec, "sclk_hz": hz}
@@ -68,15 +77,17 @@ def measure(target_sec: float = 0.15) -> list:
     lib = load()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     out = []
-    for waves in (1, 2, 4):
+    for kind, waves in ((0, 1), (0, 2), (0, 4), (1, 2), (2, 2), (3, 2), (4, 2)):
+        name, peak = KINDS[kind]
         block = 256 * waves
-        run(lib, cus, block, 1000)                              # warm-up
-        probe = run(lib, cus, block, 20000)
+        run(lib, cus, block, 1000, kind)                        # warm-up
+        probe = run(lib, cus, block, 20000, kind)
         iters = max(1000, int(20000 * target_sec / probe["sec"]))
-        r = run(lib, cus, block, iters)
+        r = run(lib, cus, block, iters, kind)
         hz = r["sclk_hz"]
-        out.append({"waves_per_simd": waves, "grid": cus, "block": block, "iters": iters,
-                    "ms": r["sec"] * 1e3, "pops": r["pops"], "frac": r["pops"] / PEAK_INT8_POPS,
+        out.append({"inst": name, "waves_per_simd": waves, "grid": cus, "block": block,
+                    "iters": iters, "ms": r["sec"] * 1e3, "pops": r["pops"],
+                    "frac": r["pops"] / peak,
                     "sclk_ghz_median": statistics.median(hz) / 1e9,
                     "sclk_ghz_min": min(hz) / 1e9, "sclk_ghz_max": max(hz) / 1e9})
     return out
@@ -90,10 +101,10 @@ def main(argv=None) -> int:
     import torch
     rows = measure()
     name = torch.cuda.get_device_properties(0).name
-    lines = ["# MFMA-only rate of v_mfma_i32_32x32x32_i8 (4 independent chains per wave, one "
-             "workgroup per CU) and the shader clock under it",
-             "# sclk = s_memtime cycles / s_memrealtime (100 MHz) per workgroup; frac = POP/s / "
-             "5.0e15 (published dense int8 peak at 2.4 GHz)",
+    lines = ["# MFMA-only rates (4 independent chains per wave, one workgroup per CU) and the "
+             "shader clock under them",
+             "# sclk = s_memtime cycles / s_memrealtime (100 MHz) per workgroup; frac = rate / "
+             "published dense peak of the type at 2.4 GHz (int8 5.0e15, fp4 10.1e15)",
              f"# command (repository root): {a.command}",
              f"device={name}; cus={rows[0]['grid']}"]
     for r in rows:

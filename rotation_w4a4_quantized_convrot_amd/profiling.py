@@ -178,15 +178,16 @@ def counters_of_largest(dirs: List[str], needle: str, by: str) -> Dict[str, floa
     return out
 
 
-def read_calibration(path: str) -> Dict[int, dict]:
-    """calibration.py's summary: waves per SIMD -> {pops, sclk_ghz_median, ...}."""
+def read_calibration(path: str, inst: str = "i8_32x32x32") -> Dict[int, dict]:
+    """calibration.py's summary for one instruction: waves per SIMD -> {pops, sclk_ghz_median,
+    ...}."""
     out = {}
     with open(path) as f:
         for line in f:
-            if not line.startswith("waves_per_simd="):
+            if not line.startswith(f"inst={inst};"):
                 continue
             d = {}
-            for part in line.strip().split("; "):
+            for part in line.strip().split("; ")[1:]:
                 k, _, v = part.partition("=")
                 d[k] = float(v)
             out[int(d["waves_per_simd"])] = d

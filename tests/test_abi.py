@@ -284,34 +284,22 @@ def test_fused_linear_validates_before_launch(lib):
 
 
 def test_calibration_library_exports():
-    """libconvrot_calib.so (built with the layer's library) exports its three calls, and the
-    launcher rejects bad shapes before touching the device."""
+    """libconvrot_calib.so (built with the layer's library) exports its calls, and the
+    launcher rejects bad arguments before touching the device."""
     import ctypes
     from rotation_w4a4_quantized_convrot_amd import calibration as C
     if not os.path.exists(C.CALIB_PATH):
         pytest.skip("libconvrot_calib.so not built")
     lib = C.load()
-    assert lib.convrot_calib_macs_per_mfma() == 32 * 32 * 32
+    assert lib.convrot_calib_ops_per_inst(0) == 2 * 32 * 32 * 32
+    assert lib.convrot_calib_ops_per_inst(1) == 2 * 32 * 32 * 64
+    assert lib.convrot_calib_ops_per_inst(2) == 2 * 16 * 16 * 128
+    assert lib.convrot_calib_ops_per_inst(3) == lib.convrot_calib_ops_per_inst(4) == 2 * 32 ** 3
+    assert lib.convrot_calib_ops_per_inst(5) == 0
     assert lib.convrot_calib_chains() >= 1
-    bad = [(0, 256, 1), (1, 100, 1), (1, 2048, 1), (1, 256, -1)]
-    for grid, block, iters in bad:
-        assert lib.convrot_calib_mfma_i8(grid, block, iters, ctypes.c_void_p(16),
-                                         ctypes.c_void_p(16), None) != 0
-    assert lib.convrot_calib_mfma_i8(1, 256, 1, None, ctypes.c_void_p(16), None) != 0
-
-
-def test_row_quant_helpers_validate(lib):
-    """Shape, NULL and alignment errors come back before anything is enqueued."""
-    import ctypes
-    p = ctypes.c_void_p(64)
-    assert lib.convrot_quant_rows_int4(p, -1, 8, 8, p, p, None) == _lib.CONVROT_ERR_SHAPE
-    assert lib.convrot_quant_rows_int4(p, 4, 8, 7, p, p, None) == _lib.CONVROT_ERR_SHAPE
-    assert lib.convrot_quant_rows_int4(p, 4, 0, 8, p, p, None) == _lib.CONVROT_ERR_SHAPE
-    assert lib.convrot_quant_rows_int4(None, 4, 8, 8, p, p, None) == _lib.CONVROT_ERR_NULL
-    assert lib.convrot_quant_rows_int4(ctypes.c_void_p(66), 4, 8, 8, p, p, None) == \
-        _lib.CONVROT_ERR_ALIGN
-    assert lib.convrot_quant_rows_int4(p, 0, 8, 8, None, None, None) == _lib.CONVROT_OK
-    assert lib.convrot_dequant_int4(p, p, 4, 0, p, None) == _lib.CONVROT_ERR_SHAPE
-    assert lib.convrot_dequant_int4(p, p, 1 << 40, 2, p, None) == _lib.CONVROT_ERR_SHAPE
-    assert lib.convrot_dequant_int4(p, None, 4, 8, p, None) == _lib.CONVROT_ERR_NULL
-    assert lib.convrot_dequant_int4(p, p, 4, 8, ctypes.c_void_p(68), None) == _lib.CONVROT_ERR_ALIGN
+    bad = [(0, 0, 256, 1), (0, 1, 100, 1), (0, 1, 2048, 1), (0, 1, 256, -1), (5, 1, 256, 1),
+           (-1, 1, 256, 1)]
+    for kind, grid, block, iters in bad:
+        assert lib.convrot_calib_mfma(kind, grid, block, iters, ctypes.c_void_p(16),
+                                      ctypes.c_void_p(16), None) != 0
+    assert lib.convrot_calib_mfma(0, 1, 256, 1, None, ctypes.c_void_p(16), None) != 0

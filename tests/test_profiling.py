@@ -120,8 +120,9 @@ def test_counter_summary_derivations(tmp_path):
     cal_txt = tmp_path / "mfma_peak_sclk.txt"
     ops = 2 * M * N * Kp / 1e-6
     cal_txt.write_text("# header\ndevice=x; cus=256\n"
-                       "waves_per_simd=1; pops=1e15; sclk_ghz_median=1.5\n"
-                       f"waves_per_simd=2; pops={4 * ops}; sclk_ghz_median=2.0\n")
+                       "inst=i8_32x32x32; waves_per_simd=1; pops=1e15; sclk_ghz_median=1.5\n"
+                       f"inst=i8_32x32x32; waves_per_simd=2; pops={4 * ops}; sclk_ghz_median=2.0\n"
+                       "inst=fp4_32x32x64_scaled; waves_per_simd=2; pops=1e12; sclk_ghz_median=1.0\n")
     lines = P.counter_summary([str(tmp_path / "pmc")], [str(tmp_path / "cal")], str(stats),
                               str(cal_txt), M, N, Kp, 256)
     text = "\n".join(lines)
@@ -136,9 +137,13 @@ def test_counter_summary_derivations(tmp_path):
 
 def test_read_calibration(tmp_path):
     p = tmp_path / "c.txt"
-    p.write_text("# x\ndevice=d; cus=256\nwaves_per_simd=2; grid=256; pops=4.9e+15; sclk_ghz_median=2.38\n")
+    p.write_text("# x\ndevice=d; cus=256\n"
+                 "inst=i8_32x32x32; waves_per_simd=2; grid=256; pops=4.9e+15; sclk_ghz_median=2.38\n"
+                 "inst=fp4_32x32x64_scaled; waves_per_simd=2; grid=256; pops=7e+15; sclk_ghz_median=2.1\n")
     c = P.read_calibration(str(p))
     assert set(c) == {2} and c[2]["pops"] == 4.9e15 and c[2]["sclk_ghz_median"] == 2.38
+    f = P.read_calibration(str(p), "fp4_32x32x64_scaled")
+    assert f[2]["pops"] == 7e15
 
 
 def test_source_hash_covers_device_headers():
