@@ -72,7 +72,7 @@ void fused_linear_kernel(const uint16_t* __restrict__ x, int M, int K, int Kp, i
                          uint16_t* __restrict__ y, unsigned* __restrict__ fail) {
   constexpr int kSt = big::stage_bytes<4>();
   __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kSt];
-  __shared__ __attribute__((aligned(16))) float fac[3 * big::kBM];
+  __shared__ __attribute__((aligned(16))) float fac[big::kFacFloats];
   rht_quant_body<G, uint16_t, 16, kFmtInt4>(x, M, K, long(K), Kp, W, R, nblocks, xq, xs, nullptr,
                                             nullptr, reinterpret_cast<uint32_t*>(lds),
                                             blockIdx.x, gridDim.x);
@@ -82,7 +82,7 @@ void fused_linear_kernel(const uint16_t* __restrict__ x, int M, int K, int Kp, i
     __syncthreads();  // the previous tile's epilogue has finished with the stage buffers
     big::gemm_tile_body<false, 4>(xq, xs, wq, ws, nullptr, nullptr, bias, M, N, Kp, tiles_m,
                                   tiles_n, y, nullptr, lds, lds + kSt, lds + 2 * kSt,
-                                  lds + 3 * kSt, fac, bid);
+                                  lds + 3 * kSt, nullptr, fac, bid);
   }
 }
 

@@ -33,6 +33,9 @@ constexpr int kWaves = 8;                      // two waves per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 256, kBN = 256;            // workgroup tile along m (activations) and n
 constexpr int kWavesN = 2, kWavesM = kWaves / kWavesN;
+// Epilogue factors in LDS: activation scales, weight scales, bias, kThreads floats each (one
+// per thread, so that every thread stores without a condition; the first 256 are the tile's).
+constexpr int kFacFloats = 3 * kThreads;
 constexpr int kTM = kBM / kWavesM, kTN = kBN / kWavesN;  // wave tile
 constexpr int kGM = kTM / 32, kGN = kTN / 32;  // 32-row MFMA blocks per wave
 constexpr int kAStage = kBM * kBKB;            // bytes of activation codes per stage
@@ -44,14 +47,21 @@ constexpr int kDmaPerWave = kDma / kWaves;
 constexpr uint32_t kOob = 0x80000000u;
 
 // Code formats (QB): 4 = packed int4, 8 = int8, kQbMx = MXFP4 (packed E2M1 codes, like int4,
-// plus one E8M0 byte per 32 codes).  MXFP4 stages also hold each row's four scale bytes of
-// the step (A rows then B rows, one dword per row), moved by one extra 256-byte transfer per
-// wave, and accumulate in fp32 on v_mfma_scale_f32_32x32x64_f8f6f4.
+// plus one E8M0 byte per 32 codes), accumulated in fp32 on v_mfma_scale_f32_32x32x64_f8f6f4.
+// Each MXFP4 stage has a scale area beside it: the rows' four scale bytes of the step (A rows
+// then B rows, one dword per row).  The scales are loaded four steps at a time, 16 bytes per
+// row into registers, and each refill writes its step's dword with an LDS store before the
+// stage's code transfers go out.  (Moving them with a 4-byte buffer-to-LDS transfer per row
+// and step touched as many cache lines as the codes themselves: without those transfers the
+// kernel measured 26.5 against 32.4 us at attention-projection size.)  The four areas are one
+// LDS object of their own, apart from the stage buffers: the compiler orders an LDS store
+// after every transfer still in flight into the same object.
 constexpr int kQbMx = 1;
-constexpr int kScaleStage = 4 * (kBM + kBN);
+constexpr int kScaleDwords = kBM + kBN;  // one scale area
+constexpr int kScaleGroup = 4;           // K steps of scales per load
 template <int QB> constexpr int code_bits() { return QB == 8 ? 8 : 4; }
-template <int QB> constexpr int stage_bytes() { return kStage + (QB == kQbMx ? kScaleStage : 0); }
-template <int QB> constexpr int dma_per_wave() { return kDmaPerWave + (QB == kQbMx ? 1 : 0); }
+template <int QB> constexpr int stage_bytes() { return kStage; }
+template <int QB> constexpr int dma_per_wave() { return kDmaPerWave; }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -88,17 +98,6 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t 
                                             __amdgpu_buffer_rsrc_t rsb, int rowB, int srow,
                                             int step, int wave, int lane) {
   const int kb = step * kBKB;
-  if constexpr (QB == kQbMx) {
-    // scale dwords of rows 64 t .. 64 t + 63 (t = wave % 4): A for waves 0-3, B for 4-7
-    const int t = wave & 3;
-    const uint32_t off = 4 * step < srow ? uint32_t((64 * t + lane) * srow + 4 * step) : kOob;
-    if (wave < 4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr)(st + kStage + 256 * t), 4, off, 0,
-                                               0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr)(st + kStage + 4 * kBM + 256 * t),
-                                               4, off, 0, 0, 0);
-  }
 #pragma unroll
   for (int i = 0; i < kDmaA / kWaves; ++i) {
     const int g = wave + kWaves * i;
@@ -114,6 +113,32 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t 
 }
 
 
+// MXFP4 scales: 16 bytes (the scale dwords of K steps 4 group .. 4 group + 3) of rows
+// 64 t .. 64 t + 63 (t = wave % 4; activation rows for waves 0-3, weight rows for 4-7), one
+// row per lane.  Buffer range checks are per dword, so a row's last group returns its real
+// bytes even where its 16 bytes run past the end of the scales.  The K loop's vmcnt waits
+// count this load at the place it is written, between two stages' transfers; the empty asm
+// statements with a memory clobber keep the compiler from moving it (it reads memory that
+// the transfers do not write, and would otherwise be free to go anywhere).
+__device__ __forceinline__ uint4 load_scales(__amdgpu_buffer_rsrc_t rsa,
+                                             __amdgpu_buffer_rsrc_t rsb, int srow, int group,
+                                             int wave, int lane) {
+  const int t = wave & 3;
+  const int byte = 4 * kScaleGroup * group;
+  const uint32_t off = byte < srow ? uint32_t((64 * t + lane) * srow + byte) : kOob;
+  asm volatile("" ::: "memory");
+  const uint4 v = __builtin_bit_cast(
+      uint4, __builtin_amdgcn_raw_buffer_load_b128(wave < 4 ? rsa : rsb, off, 0, 0));
+  asm volatile("" ::: "memory");
+  return v;
+}
+
+// The scale dword of one step for this wave's 64 rows, into a stage's scale area.
+__device__ __forceinline__ void store_scale(uint32_t* sc, uint32_t v, int wave, int lane) {
+  const int t = wave & 3;
+  sc[(wave < 4 ? 0 : kBM) + 64 * t + lane] = v;
+}
+
 // Half of one K step's fragments: one 16-byte chunk per lane and 32-row block.  For a block,
 // lane l reads row l % 32 (h = l / 32).  int4: chunk 2h + c, i.e. codes 64h + 32c .. + 31,
 // feeding MFMA substeps 2c and 2c + 1; int8: chunk 2c + h, feeding substep c.  Weights and
@@ -127,13 +152,13 @@ struct Half {
 };
 
 template <int QB>
-__device__ __forceinline__ void read_half(const uint8_t* st, int c, int wn, int wm, int lane,
-                                          Half& f) {
+__device__ __forceinline__ void read_half(const uint8_t* st, const uint32_t* sc, int c, int wn,
+                                          int wm, int lane, Half& f) {
   const int r32 = lane & 31, h = lane >> 5;
   const int q = QB == 4 ? 2 * h + c : 2 * c + h;
   if (QB == kQbMx && c == 0) {
-    const uint32_t* SA = reinterpret_cast<const uint32_t*>(st + kStage);
-    const uint32_t* SB = SA + kBM;
+    const uint32_t* SA = sc;
+    const uint32_t* SB = sc + kBM;
 #pragma unroll
     for (int j = 0; j < kGM; ++j) f.sx[j] = SA[wm * kTM + 32 * j + r32] >> (8 * h);
 #pragma unroll
@@ -281,8 +306,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
                                          uint16_t* __restrict__ y,
                                          int32_t* __restrict__ acc_dbg) {
   constexpr int kPitch = 272;
-  const float* fw = fx + kBM;
-  const float* fb = fw + kBN;
+  const float* fw = fx + kThreads;
+  const float* fb = fw + kThreads;
   const int wn = wave & 1, wm = wave >> 1;
   const int r32 = lane & 31;
   // Each wave's 32 x 128 staging rows: three per stage buffer.
@@ -343,7 +368,8 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
 // kernel's register allocation free of the extra live values).  QB: code width, 4 (packed
 // int4, K'/2 bytes per row) or 8 (int8, K' bytes per row).
 // One 256 x 256 tile of the output.  st0..st3: the four stages of the operand ring
-// (stage_bytes<QB>() each), fac: 3 * 256 floats of LDS; bid / nbid: this workgroup's index in
+// (stage_bytes<QB>() each), scl: MXFP4 only, their scale areas (4 kScaleDwords dwords of LDS,
+// another object), fac: kFacFloats floats of LDS; bid / nbid: this workgroup's index in
 // a grid of 8 * ceil(tiles / 8) workgroups (or more: the surplus ones return at once).
 template <bool kDbg, int QB>
 __device__ __forceinline__ void gemm_tile_body(
@@ -351,7 +377,8 @@ __device__ __forceinline__ void gemm_tile_body(
     const float* __restrict__ ws, const uint8_t* __restrict__ xbs,
     const uint8_t* __restrict__ wbs, const uint16_t* __restrict__ bias, int M, int N, int Kp,
     int tiles_m, int tiles_n, uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg,
-    uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3, float* fac, int bid) {
+    uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3, uint32_t* scl, float* fac,
+    int bid) {
   constexpr int kDpw = dma_per_wave<QB>();
   // XCD-grouped tile order: blocks are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous range of tiles, walked four tile-rows at a time.
@@ -381,15 +408,19 @@ __device__ __forceinline__ void gemm_tile_body(
   const int srow = ((Kp + 127) >> 7) * 4;       // MXFP4: bytes of block scales per row
   const int nsteps = (rowB + kBKB - 1) / kBKB;
   // Epilogue factors, requested now so that their latency hides behind the first stages.
-  float xsv, wsv;
-  uint32_t bbits;  // bf16 bits of the bias; -0.0 (0x8000) when there is none
+  // They are buffer loads (a row or column past the end reads 0), issued without a branch:
+  // loaded under a condition, the bias was shifted inside the branch, and the compiler waited
+  // for it there, before the first stage's transfers had gone out.
+  uint32_t xsv = 0u, wsv = 0u, bld;
+  const bool has_bias = bias != nullptr;
   {
-    const int tid = wave * 64 + lane;  // one row and one column of the tile per thread
-    const long mx = m0 + tid, nx = n0 + tid;
-    const bool own = tid < kBM;
-    xsv = QB != kQbMx && own && mx < M ? xs[mx] : 0.f;
-    wsv = QB != kQbMx && own && nx < N ? ws[nx] : 0.f;
-    bbits = (own && bias != nullptr && nx < N) ? uint32_t(bias[nx]) : 0x8000u;
+    const uint32_t off = uint32_t(wave * 64 + lane);  // one row and one column per thread
+    if constexpr (QB != kQbMx) {
+      xsv = __builtin_amdgcn_raw_buffer_load_b32(rsrc(xs + m0, (long(M) - m0) * 4), 4 * off, 0, 0);
+      wsv = __builtin_amdgcn_raw_buffer_load_b32(rsrc(ws + n0, (long(N) - n0) * 4), 4 * off, 0, 0);
+    }
+    bld = __builtin_amdgcn_raw_buffer_load_b16(
+        rsrc(has_bias ? bias + n0 : bias, has_bias ? (long(N) - n0) * 2 : 0), 2 * off, 0, 0);
   }
   const __amdgpu_buffer_rsrc_t ra = rsrc(xq + m0 * rowB, (long(M) - m0) * rowB);
   const __amdgpu_buffer_rsrc_t rb = rsrc(wq + n0 * rowB, (long(N) - n0) * rowB);
@@ -417,28 +448,49 @@ __device__ __forceinline__ void gemm_tile_body(
   // lets the compiler keep the newer transfers in flight.
   Half f0, f1, g0;
   Unp u0;  // int4: substep 0 of the current stage, unpacked before the step's barrier
+  // MXFP4 scale registers: sa holds group 0 (steps 0-3), p and q the groups that the two
+  // halves of the K loop below write into their stages.  sa goes out before stage 0 and p
+  // between stages 1 and 2; the wait for stage 0 then leaves stage 1's and 2's transfers and
+  // p in flight.
+  uint4 sa = {0u, 0u, 0u, 0u}, p = {0u, 0u, 0u, 0u}, q = {0u, 0u, 0u, 0u};
+  uint32_t* const sc0 = scl;
+  uint32_t* const sc1 = scl + kScaleDwords;
+  uint32_t* const sc2 = scl + 2 * kScaleDwords;
+  uint32_t* const sc3 = scl + 3 * kScaleDwords;
+  if constexpr (QB == kQbMx) sa = load_scales(rsa, rsb, srow, 0, wave, lane);
   issue_stage<QB>(st0, ra, rb, rsa, rsb, rowB, srow, 0, wave, lane);
   issue_stage<QB>(st1, ra, rb, rsa, rsb, rowB, srow, 1, wave, lane);
+  if constexpr (QB == kQbMx) p = load_scales(rsa, rsb, srow, 1, wave, lane);
   issue_stage<QB>(st2, ra, rb, rsa, rsb, rowB, srow, 2, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDpw));  // vmcnt: stage 0 landed
+  if constexpr (QB == kQbMx) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDpw + 1));  // vmcnt: stage 0 (and sa) landed
+    store_scale(sc0, sa.x, wave, lane);
+    store_scale(sc1, sa.y, wave, lane);
+    store_scale(sc2, sa.z, wave, lane);
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDpw));  // vmcnt: stage 0 landed
+  }
   {
     const int tid = wave * 64 + lane;
-    if (tid < kBM) {  // kBM == kBN; the epilogue reads these after the K loop's barriers
-      fac[tid] = xsv;
-      fac[kBM + tid] = wsv;
-      fac[2 * kBM + tid] = __uint_as_float(bbits << 16);  // bf16 -> fp32 is exact
-    }
+    // the epilogue reads these after the K loop's barriers; no bias: -0.0 (0x8000), which
+    // leaves every sum unchanged, -0.0 included
+    const uint32_t bbits = has_bias ? uint32_t(bld) : 0x8000u;
+    fac[tid] = __uint_as_float(xsv);
+    fac[kThreads + tid] = __uint_as_float(wsv);
+    fac[2 * kThreads + tid] = __uint_as_float(bbits << 16);  // bf16 -> fp32 is exact
   }
+  // MXFP4: stage 0's scales, just stored, are read right after the barrier by every wave
+  if constexpr (QB == kQbMx) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
-  read_half<QB>(st0, 0, wn, wm, lane, f0);
+  read_half<QB>(st0, sc0, 0, wn, wm, lane, f0);
   if constexpr (QB == 4) unpack_sub(f0, 0, u0);
 #define CONVROT_STEP(K, CUR, NEXT, REFILL)                                          \
   __builtin_amdgcn_s_waitcnt(0x0F70 | kDpw);        /* vmcnt: stage K + 1 landed */  \
   __builtin_amdgcn_s_waitcnt(0xC07F);               /* lgkmcnt(0) */                \
   __builtin_amdgcn_s_barrier();                                                     \
   issue_stage<QB>(REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);       \
-  read_half<QB>(CUR, 1, wn, wm, lane, f1);                                          \
-  read_half<QB>(NEXT, 0, wn, wm, lane, g0);                                         \
+  read_half<QB>(CUR, nullptr, 1, wn, wm, lane, f1);                                 \
+  read_half<QB>(NEXT, nullptr, 0, wn, wm, lane, g0);                                \
   if constexpr (QB == 4) {                                                          \
     mma_unp(u0, acc);                                                               \
     Unp u;                                                                          \
@@ -452,6 +504,71 @@ __device__ __forceinline__ void gemm_tile_body(
   }                                                                                 \
   f0 = g0;
   int k = 0;
+  if constexpr (QB == kQbMx) {
+    // Step K refills stage K + 3 and writes its scale dword, (K + 3) % 4 of group (K + 3) / 4.
+    // Step 0 runs on its own and loads q; the loop then takes eight steps k .. k + 7 with
+    // k = 1 (mod 8): the first four write group (k + 3) / 4 from p, the last four the next
+    // group from q, and each quad is reloaded, two groups on, right after its last use, so
+    // that no register has to move between the two.  VM: the memory operations issued after
+    // stage K + 1's transfers (stage K + 2's, and a scale load issued right after stage K + 1's
+    // or K + 2's transfers), which may still be in flight when stage K + 1 has landed.
+#define CONVROT_STEP_MX(K, CUR, NEXT, REFILL, SV, VM)                                    \
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (VM));         /* vmcnt: stage K + 1 landed */  \
+  __builtin_amdgcn_s_waitcnt(0xC07F);                /* lgkmcnt(0) */                \
+  __builtin_amdgcn_s_barrier();                                                      \
+  store_scale(sc##REFILL, SV, wave, lane);                                           \
+  issue_stage<QB>(st##REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);    \
+  read_half<QB>(st##CUR, nullptr, 1, wn, wm, lane, f1);                              \
+  read_half<QB>(st##NEXT, sc##NEXT, 0, wn, wm, lane, g0);                            \
+  mma_half<QB, 0>(f0, f0, acc);                                                      \
+  mma_half<QB, 1>(f1, f0, acc);                                                      \
+  f0 = g0;
+    // nsteps >= 1 (every entry point rejects K < 1), so step 0 always runs; had the loop a
+    // way in that skipped it, the compiler would wait there for transfers that step 0 has
+    // long seen land.
+    {
+      CONVROT_STEP_MX(0, 0, 1, 3, sa.w, kDpw + 1)
+      q = load_scales(rsa, rsb, srow, 2, wave, lane);
+      k = 1;
+      for (; k + 8 <= nsteps; k += 8) {
+        const int g = (k + 3) / kScaleGroup;
+        CONVROT_STEP_MX(k, 1, 2, 0, p.x, kDpw + 1)
+        CONVROT_STEP_MX(k + 1, 2, 3, 1, p.y, kDpw + 1)
+        CONVROT_STEP_MX(k + 2, 3, 0, 2, p.z, kDpw)
+        CONVROT_STEP_MX(k + 3, 0, 1, 3, p.w, kDpw)
+        p = load_scales(rsa, rsb, srow, g + 2, wave, lane);
+        CONVROT_STEP_MX(k + 4, 1, 2, 0, q.x, kDpw + 1)
+        CONVROT_STEP_MX(k + 5, 2, 3, 1, q.y, kDpw + 1)
+        CONVROT_STEP_MX(k + 6, 3, 0, 2, q.z, kDpw)
+        CONVROT_STEP_MX(k + 7, 0, 1, 3, q.w, kDpw)
+        q = load_scales(rsa, rsb, srow, g + 3, wave, lane);
+      }
+      // At most seven steps left; p is not reloaded here, so steps k + 4 and k + 5 wait for
+      // stage K + 2's transfers alone.
+      if (k < nsteps) {
+        CONVROT_STEP_MX(k, 1, 2, 0, p.x, kDpw + 1)
+        if (k + 1 < nsteps) {
+          CONVROT_STEP_MX(k + 1, 2, 3, 1, p.y, kDpw + 1)
+          if (k + 2 < nsteps) {
+            CONVROT_STEP_MX(k + 2, 3, 0, 2, p.z, kDpw)
+            if (k + 3 < nsteps) {
+              CONVROT_STEP_MX(k + 3, 0, 1, 3, p.w, kDpw)
+              if (k + 4 < nsteps) {
+                CONVROT_STEP_MX(k + 4, 1, 2, 0, q.x, kDpw)
+                if (k + 5 < nsteps) {
+                  CONVROT_STEP_MX(k + 5, 2, 3, 1, q.y, kDpw)
+                  if (k + 6 < nsteps) {
+                    CONVROT_STEP_MX(k + 6, 3, 0, 2, q.z, kDpw)
+                  }
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+#undef CONVROT_STEP_MX
+  } else {
   for (; k + 4 <= nsteps; k += 4) {
     CONVROT_STEP(k, st0, st1, st3)
     CONVROT_STEP(k + 1, st1, st2, st0)
@@ -467,12 +584,17 @@ __device__ __forceinline__ void gemm_tile_body(
       }
     }
   }
+  }
 #undef CONVROT_STEP
 
   // Epilogue, staged through LDS so that global stores are whole rows.  The last steps
   // issued zero-filling transfers after their final wait: drain them before the stage
   // buffers are reused.
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  // q's last dword is never used after the K loop; kept live up to here, its register is not
+  // handed to anything else while the load into it may still be in flight (a wait for every
+  // transfer at the start of the remaining steps).
+  if constexpr (QB == kQbMx) asm volatile("" ::"v"(q.w));
   __builtin_amdgcn_s_barrier();
   epilogue<kDbg, QB>(acc, st0, st1, st2, fac, M, N, m0, n0, wave, lane, y, acc_dbg);
 }

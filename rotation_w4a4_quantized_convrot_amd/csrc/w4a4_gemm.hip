@@ -187,12 +187,13 @@ void quant_gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__
                        int32_t* __restrict__ acc_dbg) {
   constexpr int kSt = stage_bytes<QB>();
   __shared__ __attribute__((aligned(16))) uint8_t st0[kSt], st1[kSt], st2[kSt], st3[kSt];
+  __shared__ __attribute__((aligned(16))) uint32_t scl[QB == kQbMx ? 4 * kScaleDwords : 1];
   // The tile's dequantization factors (activation scales, weight scales, bias as fp32),
   // parked here once the first stage has landed so that no register holds them across the
   // K loop.
-  __shared__ __attribute__((aligned(16))) float fac[3 * kBM];
+  __shared__ __attribute__((aligned(16))) float fac[kFacFloats];
   gemm_tile_body<kDbg, QB>(xq, xs, wq, ws, xbs, wbs, bias, M, N, Kp, tiles_m, tiles_n, y,
-                           acc_dbg, st0, st1, st2, st3, fac, blockIdx.x);
+                           acc_dbg, st0, st1, st2, st3, scl, fac, blockIdx.x);
 }
 
 }  // namespace big
