@@ -16,6 +16,11 @@ it).  For each it reports:
 The published peak assumes 2.4 GHz; at a lower sustained clock the reachable rate scales
 with it, which is what the clock column is for.  Needs a GPU; loads only the calibration
 library (the oracle and the layer's library are not involved).
+
+``--gemm-tiles`` instead times the layer library's W4A4 GEMM (convrot_w4a4_gemm, the 256 x 256
+tiled kernel) at K' = 3072 and output shapes of 64 to 256 tiles, one tile per compute unit,
+with codes drawn uniformly from [-7, 7] (the range the quantizer produces): how the time of
+one tile, and the chip's aggregate rate, change with the number of compute units at work.
 """
 from __future__ import annotations
 
@@ -93,20 +98,79 @@ def measure(target_sec: float = 0.15) -> list:
     return out
 
 
+# (M, N) at K' = 3072: 64, 144, 216, 224, 255 and 256 tiles of 256 x 256 (attention
+# projection, 4608 x 3072, is the 216)
+GEMM_TILE_SHAPES = ((2048, 2048), (3072, 3072), (4608, 3072), (4096, 3584), (4352, 3840),
+                    (4096, 4096))
+
+
+def gemm_tiles(kp: int = 3072, launches: int = 200, batches: int = 5, ramp_sec: float = 0.3,
+               seed: int = 0) -> list:
+    """Median per-launch time of convrot_w4a4_gemm at GEMM_TILE_SHAPES (back-to-back launches
+    after a ramp), with the aggregate rate in POP/s."""
+    import time
+    import torch
+    import rotation_w4a4_quantized_convrot_amd as cr
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+
+    def codes(rows):  # two nibbles per byte, each uniform over [-7, 7] (two's complement)
+        q = torch.randint(-7, 8, (rows, kp), generator=gen, dtype=torch.int16) & 0xF
+        return (q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8).to(dev)
+
+    out = []
+    for M, N in GEMM_TILE_SHAPES:
+        xq, wq = codes(M), codes(N)
+        xs = (torch.rand(M, generator=gen) * 1e-2 + 1e-3).to(dev)
+        ws = (torch.rand(N, generator=gen) * 1e-2 + 1e-3).to(dev)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        t0 = time.time()
+        while time.time() - t0 < ramp_sec:
+            for _ in range(20):
+                cr.convrot_w4a4_gemm(xq, xs, wq, ws, None, y)
+            torch.cuda.synchronize()
+        per = []
+        for _ in range(batches):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(launches):
+                cr.convrot_w4a4_gemm(xq, xs, wq, ws, None, y)
+            b.record()
+            b.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / launches)
+        us = statistics.median(per)
+        tiles = -(-M // 256) * -(-N // 256)
+        out.append({"M": M, "N": N, "Kp": kp, "tiles": tiles, "us": us,
+                    "pops": 2.0 * M * N * kp / (us * 1e-6) / 1e15})
+    return out
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
     p.add_argument("--out", default=None, help="write the summary here as well")
-    p.add_argument("--command", default="python -m rotation_w4a4_quantized_convrot_amd.calibration")
+    p.add_argument("--command", default=None, help="the command line to record in the summary")
+    p.add_argument("--gemm-tiles", action="store_true",
+                   help="time the W4A4 GEMM at 64 to 256 tiles instead (layer library)")
     a = p.parse_args(argv)
+    if a.command is None:
+        a.command = "python -m rotation_w4a4_quantized_convrot_amd.calibration" + (
+            " --gemm-tiles" if a.gemm_tiles else "")
     import torch
-    rows = measure()
     name = torch.cuda.get_device_properties(0).name
-    lines = ["# MFMA-only rates (4 independent chains per wave, one workgroup per CU) and the "
-             "shader clock under them",
-             "# sclk = s_memtime cycles / s_memrealtime (100 MHz) per workgroup; frac = rate / "
-             "published dense peak of the type at 2.4 GHz (int8 5.0e15, fp4 10.1e15)",
-             f"# command (repository root): {a.command}",
-             f"device={name}; cus={rows[0]['grid']}"]
+    if a.gemm_tiles:
+        rows = gemm_tiles()
+        lines = ["# W4A4 GEMM (256 x 256 tiles, one per CU) at K' = 3072, codes uniform in "
+                 "[-7, 7]: median per-launch time of 5 batches of 200 back-to-back launches",
+                 f"# command (repository root): {a.command}",
+                 f"device={name}; cus={torch.cuda.get_device_properties(0).multi_processor_count}"]
+    else:
+        rows = measure()
+        lines = ["# MFMA-only rates (4 independent chains per wave, one workgroup per CU) and "
+                 "the shader clock under them",
+                 "# sclk = s_memtime cycles / s_memrealtime (100 MHz) per workgroup; frac = "
+                 "rate / published dense peak of the type at 2.4 GHz (int8 5.0e15, fp4 10.1e15)",
+                 f"# command (repository root): {a.command}",
+                 f"device={name}; cus={rows[0]['grid']}"]
     for r in rows:
         lines.append("; ".join(f"{k}={v:.4g}" if isinstance(v, float) else f"{k}={v}"
                                for k, v in r.items()))

@@ -24,3 +24,15 @@ def test_calibration_kernel_rate_and_clock(kind):
     # clock (plus 5% for the launch-time spread between workgroups)
     peak = C.KINDS[kind][1]
     assert 0 < r["pops"] <= 1.05 * peak * clock / C.PEAK_CLOCK_HZ
+
+
+def test_gemm_tiles_mode():
+    """The GEMM tile-count timing: one row per shape, tile counts as stated, rates below the
+    published int8 peak."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rotation_w4a4_quantized_convrot_amd import calibration as C
+    print("\n[case] calibration gemm_tiles launches=5 batches=1", flush=True)
+    rows = C.gemm_tiles(launches=5, batches=1, ramp_sec=0.01)
+    assert [r["tiles"] for r in rows] == [64, 144, 216, 224, 255, 256]
+    assert all(r["us"] > 0 and 0 < r["pops"] < C.PEAK_INT8_POPS / 1e15 for r in rows)

@@ -190,6 +190,18 @@ MX_GEMM_CASES = [
 
 @pytest.mark.parametrize("M,N,Kp,with_bias", MX_GEMM_CASES)
 def test_mxfp4_gemm_parity(cr, M, N, Kp, with_bias):
+    _mx_gemm_case(cr, M, N, Kp, with_bias)
+
+
+# The tiled kernel runs K step 0 on its own, then eight steps per loop iteration, then the
+# 0-7 steps left: K' = 128 n covers n K steps, every tail length and loop counts 0, 1 and 2,
+# plus a ragged last step.
+@pytest.mark.parametrize("nsteps", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 16, 17, 9.5])
+def test_mxfp4_tiled_k_loop_lengths(cr, nsteps):
+    _mx_gemm_case(cr, 600, 3000, int(128 * nsteps), int(nsteps) % 2 == 0)
+
+
+def _mx_gemm_case(cr, M, N, Kp, with_bias):
     _announce(f"mxfp4 gemm M={M} N={N} Kp={Kp} bias={with_bias}")
     rng = np.random.default_rng(M + 5 * N + Kp)
     cx = rng.integers(0, 16, size=(M, Kp)).astype(np.uint8)
