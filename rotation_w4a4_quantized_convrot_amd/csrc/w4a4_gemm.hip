@@ -490,13 +490,13 @@ __global__ __launch_bounds__(Shape<MB>::kThreads) void quant_gemm_skinny_kernel(
 // its 96 KB, and whole-line transfers pull it faster (measured on MI355X, M = 64,
 // N = K' = 3072, back to back in a HIP graph: 5.9 against 6.6 us with the weights streamed
 // from HBM, 4.7 against 5.5 us from L2; K' = 12288: 14.4 against 17.9 us).
-//   * K goes in rounds of 1 KB of codes per row (16 K steps, one per wave), double-buffered:
-//     round r + 2 is requested into a buffer once every wave has finished reading round r.
-//   * LDS holds a round as [operand][line][row][128 B]; 16-byte slot p of row r holds chunk
+//   * K goes in batches of 1 KB of codes per row (16 K steps, one per wave), double-buffered:
+//     batch r + 2 is requested into a buffer once every wave has finished reading batch r.
+//   * LDS holds a batch as [operand][line][row][128 B]; 16-byte slot p of row r holds chunk
 //     p ^ (r % 8) of the line, so the fragment reads (eight consecutive rows, one chunk)
 //     hit eight different slots.
 //   * Fragments, unpacking and the K order are those of the other kernels; the waves'
-//     partial sums meet in LDS (the round buffers' space) and are added in wave order, which
+//     partial sums meet in LDS (the batch buffers' space) and are added in wave order, which
 //     for integer sums is exact.
 namespace skinny_lds {
 
@@ -505,15 +505,15 @@ using big::f32x2;
 using big::bf16x2;
 constexpr int kTN = 32, kTM = 32;         // output columns and activation rows per workgroup
 constexpr int kWaves = 16, kThreads = 64 * kWaves;
-constexpr int kRB = 1024;                 // bytes of codes per row per round
-constexpr int kOp = kTN * kRB;            // one operand of a round: 32 rows, 32 KB
-constexpr int kBuf = 2 * kOp;             // a round: weights, then activations
-constexpr int kTransfers = 2 * kOp / 1024 / kWaves;  // 1 KB transfers per wave per round (4)
+constexpr int kRB = 1024;                 // bytes of codes per row per batch
+constexpr int kOp = kTN * kRB;            // one operand of a batch: 32 rows, 32 KB
+constexpr int kBuf = 2 * kOp;             // a batch: weights, then activations
+constexpr int kTransfers = 2 * kOp / 1024 / kWaves;  // 1 KB transfers per wave per batch (4)
 
-// Round transfers into one round buffer: transfer t = wave + 16 i; i < 2 are weights, i >= 2
+// Batch transfers into one batch buffer: transfer t = wave + 16 i; i < 2 are weights, i >= 2
 // activations; within an operand, line t % 32 / 4 and rows 8 (t % 4) .. + 7.  Bytes past the
 // row (and rows past M or N, through the buffer range) arrive as zeros.
-__device__ __forceinline__ void issue_round(uint8_t* __restrict__ buf, __amdgpu_buffer_rsrc_t rw,
+__device__ __forceinline__ void issue_batch(uint8_t* __restrict__ buf, __amdgpu_buffer_rsrc_t rw,
                                             __amdgpu_buffer_rsrc_t rx, int rowB, int kb0,
                                             int wave, int lane) {
 #pragma unroll
@@ -530,14 +530,14 @@ __device__ __forceinline__ void issue_round(uint8_t* __restrict__ buf, __amdgpu_
   }
 }
 
-// 16-byte chunk q (0..3) of K step s of the round, row r of one operand.
+// 16-byte chunk q (0..3) of K step s of the batch, row r of one operand.
 __device__ __forceinline__ uint4 frag(const uint8_t* op, int s, int q, int r) {
   const int c = 4 * (s & 1) + q;
   return *reinterpret_cast<const uint4*>(op + 4096 * (s >> 1) + 128 * r + 16 * (c ^ (r & 7)));
 }
 
-// This wave's K step of the round in buf (wave w takes step w).
-__device__ __forceinline__ void mma_round(const uint8_t* __restrict__ buf, int rowB, int kb0, int wave,
+// This wave's K step of the batch in buf (wave w takes step w).
+__device__ __forceinline__ void mma_batch(const uint8_t* __restrict__ buf, int rowB, int kb0, int wave,
                                           int lane, v16i& acc) {
   const int nst = min(kWaves, (rowB - kb0 + kBKB - 1) / kBKB);
   if (wave >= nst) return;
@@ -552,13 +552,13 @@ __device__ __forceinline__ void mma_round(const uint8_t* __restrict__ buf, int r
   }
 }
 
-// Barriers of the round loop.  A fenced __syncthreads would also wait for the transfers of the
-// next round; instead each wave waits for its own transfers of the round about to be read
+// Barriers of the batch loop.  A fenced __syncthreads would also wait for the transfers of the
+// next batch; instead each wave waits for its own transfers of the batch about to be read
 // (vector memory counter at most VM: the operations issued after them) and a plain s_barrier
 // makes every wave's transfers visible.  The empty asm statements keep the compiler from
 // moving LDS accesses across the barrier.
 template <int VM>
-__device__ __forceinline__ void round_ready() {
+__device__ __forceinline__ void batch_ready() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | VM);  // vmcnt(VM); expcnt, lgkmcnt: no wait
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -573,7 +573,7 @@ __device__ __forceinline__ void buffer_free() {
   asm volatile("" ::: "memory");
 }
 
-// The kernel body, inlined into the kernel (two separate LDS arrays for the round buffers).
+// The kernel body, inlined into the kernel (two separate LDS arrays for the batch buffers).
 template <bool kDbg>
 __device__ __forceinline__ void skinny_lds_body(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
@@ -586,12 +586,12 @@ __device__ __forceinline__ void skinny_lds_body(
   const long nw = min(long(N) - n0, long(kTN)), mx = min(long(M) - m0, long(kTM));
   const __amdgpu_buffer_rsrc_t rw = big::rsrc(wq + n0 * rowB, nw * rowB);
   const __amdgpu_buffer_rsrc_t rx = big::rsrc(xq + m0 * rowB, mx * rowB);
-  const int nrounds = (rowB + kRB - 1) / kRB;
-  // Rounds 0 and 1 first (round 1 is all zeros when the row is shorter), then the
+  const int nbatches = (rowB + kRB - 1) / kRB;
+  // Batches 0 and 1 first (batch 1 is all zeros when the row is shorter), then the
   // dequantization factors of this thread's four outputs (row l % 32, columns
   // 8 g + 4 (l / 32) .. + 3): nine loads per wave, used only by the epilogue.
-  issue_round(buf0, rw, rx, rowB, 0, wave, lane);
-  issue_round(buf1, rw, rx, rowB, kRB, wave, lane);
+  issue_batch(buf0, rw, rx, rowB, 0, wave, lane);
+  issue_batch(buf1, rw, rx, rowB, kRB, wave, lane);
   const __amdgpu_buffer_rsrc_t rxs = big::rsrc(xs + m0, mx * 4);
   const __amdgpu_buffer_rsrc_t rws = big::rsrc(ws + n0, nw * 4);
   const __amdgpu_buffer_rsrc_t rbs = big::rsrc(bias != nullptr ? bias + n0 : nullptr,
@@ -615,35 +615,35 @@ __device__ __forceinline__ void skinny_lds_body(
                             rbs, in ? uint32_t((n - n0 + r) * 2) : big::kOob, 0, 0));
   }
 
-  // Waits count this wave's vector memory operations, which complete in issue order: a round
-  // is here once at most the operations issued after it are outstanding (for round 0 the
-  // four of round 1 and the nine factor loads; later, the four of the next round if it was
+  // Waits count this wave's vector memory operations, which complete in issue order: a batch
+  // is here once at most the operations issued after it are outstanding (for batch 0 the
+  // four of batch 1 and the nine factor loads; later, the four of the next batch if it was
   // requested).
   v16i acc = v16i{};
-  for (int rd = 0; rd < nrounds; rd += 2) {
+  for (int rd = 0; rd < nbatches; rd += 2) {
     if (rd == 0)
-      round_ready<13>();
-    else if (rd + 1 < nrounds)
-      round_ready<4>();
+      batch_ready<13>();
+    else if (rd + 1 < nbatches)
+      batch_ready<4>();
     else
-      round_ready<0>();
-    mma_round(buf0, rowB, rd * kRB, wave, lane, acc);
-    if (rd + 2 < nrounds) {
+      batch_ready<0>();
+    mma_batch(buf0, rowB, rd * kRB, wave, lane, acc);
+    if (rd + 2 < nbatches) {
       buffer_free();
-      issue_round(buf0, rw, rx, rowB, (rd + 2) * kRB, wave, lane);
+      issue_batch(buf0, rw, rx, rowB, (rd + 2) * kRB, wave, lane);
     }
-    if (rd + 1 >= nrounds) break;
-    if (rd + 2 < nrounds)
-      round_ready<4>();
+    if (rd + 1 >= nbatches) break;
+    if (rd + 2 < nbatches)
+      batch_ready<4>();
     else
-      round_ready<0>();
-    mma_round(buf1, rowB, (rd + 1) * kRB, wave, lane, acc);
-    if (rd + 3 < nrounds) {
+      batch_ready<0>();
+    mma_batch(buf1, rowB, (rd + 1) * kRB, wave, lane, acc);
+    if (rd + 3 < nbatches) {
       buffer_free();
-      issue_round(buf1, rw, rx, rowB, (rd + 3) * kRB, wave, lane);
+      issue_batch(buf1, rw, rx, rowB, (rd + 3) * kRB, wave, lane);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the factors (and round 1 when it was not read)
+  __builtin_amdgcn_s_waitcnt(0);  // the factors (and batch 1 when it was not read)
   __syncthreads();                // every wave is done reading buffer 0
   int32_t* red = reinterpret_cast<int32_t*>(buf0);   // 16 waves x 16 x 64 sums: 64 KB
 #pragma unroll
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void quant_gemm_skinny_lds_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
     const float* __restrict__ ws, const uint16_t* __restrict__ bias, int M, int N, int Kp,
     uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg) {
-  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBuf];  // two round buffers of 64 KB
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[kBuf];  // two batch buffers of 64 KB
   __shared__ __attribute__((aligned(16))) uint8_t buf1[kBuf];
   skinny_lds_body<kDbg>(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg, buf0, buf1);
 }

@@ -180,8 +180,8 @@ GEMM_CASES = [
     (1, 40, 128, True), (128, 128, 128, False), (200, 136, 1024, True), (129, 130, 256, True),
     (300, 257, 3072, False), (64, 256, 3328, True), (33, 96, 12288, False),
     (300, 7000, 3328, False), (512, 3072, 3072, True), (65, 200, 512, True),
-    # M <= 64 (LDS-staged skinny kernel): one partial round with ragged N, exactly two
-    # rounds, three rounds (an odd count, the last one half full), eight rounds
+    # M <= 64 (LDS-staged skinny kernel): one partial 1 KB batch with ragged N, exactly two
+    # batches, three batches (an odd count, the last one half full), eight batches
     (63, 2, 1056, True), (32, 33, 4096, False), (64, 3000, 5120, True), (40, 1000, 16384, False),
     # M > 512 but M N < 2^21: the skinny kernel (128-row workgroups), ragged M and N
     (1000, 1000, 512, True), (4000, 500, 256, False), (600, 3000, 320, True), (513, 4087, 96, False),
