@@ -318,9 +318,8 @@ int convrot_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq, con
                       int32_t* acc_dbg, void* stream) {
   const int st = validate_gemm(xq, xs, wq, ws, bias, M, N, Kp, y, acc_dbg);
   if (st != CONVROT_OK || M == 0 || N == 0) return st;
-  const int vec = ((Kp / 2) % 16 == 0) ? 16 : 8;
   return status_of(convrot::launch_w4a4_gemm(xq, xs, wq, ws, static_cast<const uint16_t*>(bias),
-                                             M, N, Kp, static_cast<uint16_t*>(y), acc_dbg, vec,
+                                             M, N, Kp, static_cast<uint16_t*>(y), acc_dbg,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -358,9 +357,8 @@ int convrot_w4a4_linear(const void* x, int32_t x_dtype, int64_t M, int64_t K, in
   hipError_t e = convrot::launch_rotate_quant(x, x_dtype, M, K, K, (int)g, kp, convrot::kFmtInt4,
                                               vec, xq, xs, nullptr, nullptr, s);
   if (e != hipSuccess) return CONVROT_ERR_HIP;
-  const int gvec = ((kp / 2) % 16 == 0) ? 16 : 8;
   e = convrot::launch_w4a4_gemm(xq, xs, wq, ws, static_cast<const uint16_t*>(bias), M, N, kp,
-                                static_cast<uint16_t*>(y), nullptr, gvec, s);
+                                static_cast<uint16_t*>(y), nullptr, s);
   return status_of(e);
 }
 

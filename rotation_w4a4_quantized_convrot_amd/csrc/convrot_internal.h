@@ -21,12 +21,11 @@ hipError_t launch_rotate_quant(const void* x, int x_dtype, int64_t M, int64_t K,
                                int g, int64_t Kp, int fmt, int vec_bytes, uint8_t* q, float* s,
                                uint8_t* bs, float* xrot, hipStream_t stream);
 
-// Launches the W4A4 GEMM with the fused dequant epilogue.  vec_bytes: 16 when the packed
-// row stride Kp/2 is a multiple of 16 bytes, else 8.
+// Launches the W4A4 GEMM with the fused dequant epilogue.  Kp must be a multiple of 16
+// (packed rows of a multiple of 8 bytes).
 hipError_t launch_w4a4_gemm(const uint8_t* xq, const float* xs, const uint8_t* wq,
                             const float* ws, const uint16_t* bias, int64_t M, int64_t N,
-                            int64_t Kp, uint16_t* y, int32_t* acc_dbg, int vec_bytes,
-                            hipStream_t stream);
+                            int64_t Kp, uint16_t* y, int32_t* acc_dbg, hipStream_t stream);
 
 // Launches the W8A8 GEMM (int8 codes, K' bytes per row, exact int32 sums) with the same
 // fused dequant epilogue.  Kp must be a multiple of 16.

@@ -61,9 +61,20 @@ constexpr int kScaleDwords = kBM + kBN;  // one scale area
 constexpr int kScaleGroup = 4;           // K steps of scales per load
 template <int QB> constexpr int code_bits() { return QB == 8 ? 8 : 4; }
 template <int QB> constexpr int stage_bytes() { return kStage; }
-template <int QB> constexpr int dma_per_wave() { return kDmaPerWave; }
+// kT8: rows of K'/2 = 8 (mod 16) bytes (int4 with g = 16 and an odd number of windows).
+// Every other row then starts 8 bytes off a 16-byte boundary, and a 16-byte chunk at the row's
+// end would take 8 bytes of the next row.  Those rows move in 4-byte transfers, four per
+// 16-byte slot, each range-checked on its own: four times the transfer instructions.
+template <int QB, bool kT8 = false> constexpr int dma_per_wave() {
+  return kT8 ? 4 * kDmaPerWave : kDmaPerWave;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// s_waitcnt immediate that waits until at most n vector memory operations of this wave are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
+// maxima, i.e. not waited for).
+constexpr int vm_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
 // XOR swizzle of the four 16-byte chunks of a 64-byte LDS row by bits 2-3 of the row.  A
 // ds_read_b128 is served 16 lanes at a time; with this swizzle the fragment reads (16
@@ -88,16 +99,53 @@ __device__ __forceinline__ uint32_t transfer_offset(int g, int lane, int rowB, i
   return byte < rowB ? uint32_t(row * rowB + byte) : kOob;
 }
 
+// The 4-byte form: part p of transfer g moves rows 16g + 4p .. 16g + 4p + 3; lane i fills
+// dword i % 4 of LDS slot (row i / 16, chunk (i / 4) % 4).  The swizzle stores chunk
+// ((i / 4) % 4) ^ p there (bits 2-3 of the row are p), so a lane's offset inside its row,
+// c = 16 (((i / 4) % 4) ^ p) + 4 (i % 4), depends on p alone; the rest is uniform.
+__device__ __forceinline__ int part_col4(int p, int lane) {
+  return 16 * (((lane >> 2) & 3) ^ p) + 4 * (lane & 3);
+}
+
 // This wave's transfers of one stage (A groups wave, wave + kWaves, ...; then B groups).
 // A and B address their LDS region from the stage base without selects, so the compiler
 // can tell the stages apart and keep the newer transfers in flight.
-template <int QB>
+template <int QB, bool kT8>
 __device__ __forceinline__ void issue_stage(uint8_t* st, __amdgpu_buffer_rsrc_t ra,
                                             __amdgpu_buffer_rsrc_t rb,
                                             __amdgpu_buffer_rsrc_t rsa,
                                             __amdgpu_buffer_rsrc_t rsb, int rowB, int srow,
                                             int step, int wave, int lane) {
   const int kb = step * kBKB;
+  if constexpr (kT8) {
+    // The whole offset goes in the per-lane operand, which the range check covers (rows
+    // past the operand's end read zeros).  It is formed anew for every stage from an opaque
+    // copy of the lane index: hoisted out of the K loop, the sixteen lane-constant parts
+    // would stay live in registers this kernel does not have.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int c = part_col4(p, ln);
+      const bool in_row = kb + c < rowB;
+      const uint32_t lo = uint32_t((ln >> 4) * rowB + c);
+#pragma unroll
+      for (int i = 0; i < kDmaA / kWaves; ++i) {
+        const int g = wave + kWaves * i;
+        const uint32_t u = uint32_t(__builtin_amdgcn_readfirstlane((16 * g + 4 * p) * rowB + kb));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr)(st + 1024 * g + 256 * p), 4,
+                                                 in_row ? lo + u : kOob, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kDmaB / kWaves; ++i) {
+        const int g = wave + kWaves * i;
+        const uint32_t u = uint32_t(__builtin_amdgcn_readfirstlane((16 * g + 4 * p) * rowB + kb));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr)(st + kAStage + 1024 * g + 256 * p),
+                                                 4, in_row ? lo + u : kOob, 0, 0, 0);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kDmaA / kWaves; ++i) {
     const int g = wave + kWaves * i;
@@ -371,7 +419,7 @@ __device__ __forceinline__ void epilogue(v16i (&acc)[kGN][kGM], uint8_t* st0, ui
 // (stage_bytes<QB>() each), scl: MXFP4 only, their scale areas (4 kScaleDwords dwords of LDS,
 // another object), fac: kFacFloats floats of LDS; bid / nbid: this workgroup's index in
 // a grid of 8 * ceil(tiles / 8) workgroups (or more: the surplus ones return at once).
-template <bool kDbg, int QB>
+template <bool kDbg, int QB, bool kT8 = false>
 __device__ __forceinline__ void gemm_tile_body(
     const uint8_t* __restrict__ xq, const float* __restrict__ xs, const uint8_t* __restrict__ wq,
     const float* __restrict__ ws, const uint8_t* __restrict__ xbs,
@@ -379,7 +427,7 @@ __device__ __forceinline__ void gemm_tile_body(
     int tiles_m, int tiles_n, uint16_t* __restrict__ y, int32_t* __restrict__ acc_dbg,
     uint8_t* st0, uint8_t* st1, uint8_t* st2, uint8_t* st3, uint32_t* scl, float* fac,
     int bid) {
-  constexpr int kDpw = dma_per_wave<QB>();
+  constexpr int kDpw = dma_per_wave<QB, kT8>();
   // XCD-grouped tile order: blocks are dealt to the 8 XCDs round robin; give each XCD a
   // contiguous range of tiles, walked four tile-rows at a time.
   const int T = tiles_m * tiles_n;
@@ -458,17 +506,17 @@ __device__ __forceinline__ void gemm_tile_body(
   uint32_t* const sc2 = scl + 2 * kScaleDwords;
   uint32_t* const sc3 = scl + 3 * kScaleDwords;
   if constexpr (QB == kQbMx) sa = load_scales(rsa, rsb, srow, 0, wave, lane);
-  issue_stage<QB>(st0, ra, rb, rsa, rsb, rowB, srow, 0, wave, lane);
-  issue_stage<QB>(st1, ra, rb, rsa, rsb, rowB, srow, 1, wave, lane);
+  issue_stage<QB, kT8>(st0, ra, rb, rsa, rsb, rowB, srow, 0, wave, lane);
+  issue_stage<QB, kT8>(st1, ra, rb, rsa, rsb, rowB, srow, 1, wave, lane);
   if constexpr (QB == kQbMx) p = load_scales(rsa, rsb, srow, 1, wave, lane);
-  issue_stage<QB>(st2, ra, rb, rsa, rsb, rowB, srow, 2, wave, lane);
+  issue_stage<QB, kT8>(st2, ra, rb, rsa, rsb, rowB, srow, 2, wave, lane);
   if constexpr (QB == kQbMx) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDpw + 1));  // vmcnt: stage 0 (and sa) landed
+    __builtin_amdgcn_s_waitcnt(vm_wait(2 * kDpw + 1));  // vmcnt: stage 0 (and sa) landed
     store_scale(sc0, sa.x, wave, lane);
     store_scale(sc1, sa.y, wave, lane);
     store_scale(sc2, sa.z, wave, lane);
   } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kDpw));  // vmcnt: stage 0 landed
+    __builtin_amdgcn_s_waitcnt(vm_wait(2 * kDpw));  // vmcnt: stage 0 landed
   }
   {
     const int tid = wave * 64 + lane;
@@ -485,10 +533,10 @@ __device__ __forceinline__ void gemm_tile_body(
   read_half<QB>(st0, sc0, 0, wn, wm, lane, f0);
   if constexpr (QB == 4) unpack_sub(f0, 0, u0);
 #define CONVROT_STEP(K, CUR, NEXT, REFILL)                                          \
-  __builtin_amdgcn_s_waitcnt(0x0F70 | kDpw);        /* vmcnt: stage K + 1 landed */  \
+  __builtin_amdgcn_s_waitcnt(vm_wait(kDpw));        /* vmcnt: stage K + 1 landed */  \
   __builtin_amdgcn_s_waitcnt(0xC07F);               /* lgkmcnt(0) */                \
   __builtin_amdgcn_s_barrier();                                                     \
-  issue_stage<QB>(REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);       \
+  issue_stage<QB, kT8>(REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);       \
   read_half<QB>(CUR, nullptr, 1, wn, wm, lane, f1);                                 \
   read_half<QB>(NEXT, nullptr, 0, wn, wm, lane, g0);                                \
   if constexpr (QB == 4) {                                                          \
@@ -513,11 +561,11 @@ __device__ __forceinline__ void gemm_tile_body(
     // stage K + 1's transfers (stage K + 2's, and a scale load issued right after stage K + 1's
     // or K + 2's transfers), which may still be in flight when stage K + 1 has landed.
 #define CONVROT_STEP_MX(K, CUR, NEXT, REFILL, SV, VM)                                    \
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (VM));         /* vmcnt: stage K + 1 landed */  \
+  __builtin_amdgcn_s_waitcnt(vm_wait(VM));         /* vmcnt: stage K + 1 landed */  \
   __builtin_amdgcn_s_waitcnt(0xC07F);                /* lgkmcnt(0) */                \
   __builtin_amdgcn_s_barrier();                                                      \
   store_scale(sc##REFILL, SV, wave, lane);                                           \
-  issue_stage<QB>(st##REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);    \
+  issue_stage<QB, kT8>(st##REFILL, ra, rb, rsa, rsb, rowB, srow, (K) + 3, wave, lane);    \
   read_half<QB>(st##CUR, nullptr, 1, wn, wm, lane, f1);                              \
   read_half<QB>(st##NEXT, sc##NEXT, 0, wn, wm, lane, g0);                            \
   mma_half<QB, 0>(f0, f0, acc);                                                      \

@@ -3,8 +3,9 @@
 Every kernel runs twice on the same inputs, into output buffers pre-filled with two different
 canary patterns. The two results must be bit-identical: a race would make them differ, and so
 would any output element or padding byte that a kernel leaves unwritten (it keeps its canary).
-The cases follow the kernel selection: the 256 x 256 tiled GEMM, the skinny GEMM and the
-128 x 128 GEMM, for each code format, and the rotate+quantize kernels of each format.
+The cases follow the kernel selection: the 256 x 256 tiled GEMM (also in its 4-byte transfer
+form for packed rows of 8 (mod 16) bytes) and the skinny GEMM (also with 8-byte row tails),
+for each code format, and the rotate+quantize kernels of each format.
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ GEMM_CASES = [
     # codes, M, N, Kp, kernel chosen by the library for this shape
     ("int4", 1024, 2048, 512, "tiled"), ("int4", 4000, 4090, 256, "tiled"),
     ("int4", 100, 300, 512, "skinny"),
-    ("int4", 70, 90, 48, "128x128"),
+    ("int4", 70, 90, 48, "skinny-tail8"), ("int4", 2100, 1100, 208, "tiled-4-byte"),
     ("int8", 1024, 2048, 256, "tiled"), ("int8", 100, 300, 512, "skinny"),
     ("mxfp4", 1024, 2048, 512, "tiled"), ("mxfp4", 100, 300, 512, "skinny"),
 ]

@@ -186,8 +186,11 @@ GEMM_CASES = [
     # M > 512 but M N < 2^21: the skinny kernel (128-row workgroups), ragged M and N
     (1000, 1000, 512, True), (4000, 500, 256, False), (600, 3000, 320, True), (513, 4087, 96, False),
     # K'/2 = 8 (mod 16): mid size (M N < 2^21, skinny with row tails) and large (M N >= 2^21,
-    # the 128 x 128 kernel)
+    # the tiled kernel with 4-byte transfers; the last K step holds 8, 24, 40 or 56 bytes of
+    # each row, one K step up to 25, ragged M and N)
     (1000, 1000, 528, True), (2100, 1100, 208, False), (4608, 3072, 3088, True),
+    (1100, 2000, 16, True), (1500, 1500, 48, False), (2000, 1200, 496, True),
+    (2500, 1001, 1552, False),
     # large-tile kernel (M N >= 2^21): ragged M and N, several tiles, K tails
     (600, 3500, 512, True), (1000, 2200, 1056, False), (4608, 3072, 256, True),
     (4607, 3071, 128, False), (1130, 1990, 576, True), (4000, 4090, 320, True),

@@ -42,7 +42,7 @@ def _cases(n_per_format=8, seed=2024, m_range=(1, 700), n_range=(1, 600), k_max=
     return out
 
 
-# small shapes (skinny and 128 x 128 GEMMs), then shapes large enough for the tiled GEMM
+# small shapes (skinny GEMMs), then shapes large enough for the tiled GEMM
 CASES = _cases() + _cases(n_per_format=2, seed=11, m_range=(128, 3000), n_range=(700, 3000),
                           k_max=4000) + [
     # found by a wider sweep: one activation code at a near-tie (quotient -0.4999997) moves
