@@ -42,12 +42,12 @@ RQ_SRC = ("rht_quant.hip", "rht_quant_device.h", "convrot_internal.h")
 
 # kernel key -> (substring of the demangled name, source files under csrc/)
 KERNELS = {
-    "w4a4_gemm": ("quant_gemm_kernel<false, 4>", GEMM_SRC),
-    "w8a8_gemm": ("quant_gemm_kernel<false, 8>", GEMM_SRC),
+    "w4a4_gemm": ("quant_gemm_kernel<false, 4, false>", GEMM_SRC),
+    "w8a8_gemm": ("quant_gemm_kernel<false, 8, false>", GEMM_SRC),
     "rht_quant_i4": ("rht_quant_kernel<256, unsigned short, 16, 4", RQ_SRC),
     "rht_quant_i8": ("rht_quant_kernel<256, unsigned short, 16, 8", RQ_SRC),
     "rht_quant_mx4": ("rht_quant_kernel<256, unsigned short, 16, 1", RQ_SRC),
-    "mxfp4_gemm": ("quant_gemm_kernel<false, 1>", GEMM_SRC),
+    "mxfp4_gemm": ("quant_gemm_kernel<false, 1, false>", GEMM_SRC),
 }
 CALIB_KERNEL = "mfma_i8_loop"
 

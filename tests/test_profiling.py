@@ -20,7 +20,7 @@ def _write(d, counter, rows):
                         "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": val})
 
 
-GEMM = "void convrot::(anonymous namespace)::big::quant_gemm_kernel<false, 4>(...)"
+GEMM = "void convrot::(anonymous namespace)::big::quant_gemm_kernel<false, 4, false>(...)"
 CAL = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<...>>"
 
 
