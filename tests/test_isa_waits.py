@@ -7,7 +7,8 @@ transfers in flight, a register move of a load still in flight): each shows up a
 `s_waitcnt vmcnt(0)`, a wait for every transfer, and the kernel still computes the right
 result, only slower.  These tests compile w4a4_gemm.hip to gfx950 assembly and check, for the
 production instantiations of the three code formats, that no scratch memory is used and
-that the K loop waits only for the expected counts.
+that the K loop waits only for the expected counts; and that the rotate+quantize kernels of
+the benchmarked group sizes use no scratch either.
 """
 from __future__ import annotations
 
@@ -29,17 +30,32 @@ KERNELS = {
 }
 
 
-@pytest.fixture(scope="module")
-def isa(tmp_path_factory):
+# rotate+quantize instantiations of the benchmarked workloads (bf16 input, int4 codes):
+# g = 256 (attention projection) and g = 1024 (MLP down-projection, proj_out)
+RQ_KERNELS = {"g256": "16rht_quant_kernelILi256EtLi16ELi4ELi16E",
+              "g1024": "16rht_quant_kernelILi1024EtLi16ELi4ELi8E"}
+
+
+def _assemble(tmp_path_factory, src):
     hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(hipcc):
         pytest.skip("hipcc not available")
-    out = str(tmp_path_factory.mktemp("isa") / "w4a4_gemm.s")
+    out = str(tmp_path_factory.mktemp("isa") / (src + ".s"))
     cmd = [hipcc, *B.HIPCC_FLAGS, "-I", B.INCLUDE, "-I", B.CSRC, "--cuda-device-only", "-S",
-           os.path.join(B.CSRC, "w4a4_gemm.hip"), "-o", out]
+           os.path.join(B.CSRC, src), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     with open(out) as f:
         return f.read()
+
+
+@pytest.fixture(scope="module")
+def isa(tmp_path_factory):
+    return _assemble(tmp_path_factory, "w4a4_gemm.hip")
+
+
+@pytest.fixture(scope="module")
+def rq_isa(tmp_path_factory):
+    return _assemble(tmp_path_factory, "rht_quant.hip")
 
 
 def _function(text: str, fragment: str):
@@ -81,3 +97,10 @@ def test_k_loop_waits_for_one_stage(isa, fmt):
     assert waits, f"{fmt}: no vmcnt wait in the K loop"
     assert set(waits) <= allowed, f"{fmt}: K-loop vmcnt waits {sorted(set(waits))}"
     assert all("scratch_" not in l for l in loop)
+
+
+@pytest.mark.parametrize("which", sorted(RQ_KERNELS))
+def test_rotate_quantize_no_scratch(rq_isa, which):
+    _, meta = _function(rq_isa, RQ_KERNELS[which])
+    scratch = int(re.search(r"ScratchSize:\s*(\d+)", meta).group(1))
+    assert scratch == 0, f"rotate+quantize {which}: {scratch} bytes of scratch per lane"
