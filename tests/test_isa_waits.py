@@ -8,7 +8,8 @@ transfers in flight, a register move of a load still in flight): each shows up a
 result, only slower.  These tests compile w4a4_gemm.hip to gfx950 assembly and check, for the
 production instantiations of the three code formats, that no scratch memory is used and
 that the K loop waits only for the expected counts; and that the rotate+quantize kernels of
-the benchmarked group sizes use no scratch either.
+the benchmarked group sizes use no scratch either; and that the MXFP4 kernel issues its
+scale loads where its waits count them.
 """
 from __future__ import annotations
 
@@ -104,3 +105,26 @@ def test_rotate_quantize_no_scratch(rq_isa, which):
     _, meta = _function(rq_isa, RQ_KERNELS[which])
     scratch = int(re.search(r"ScratchSize:\s*(\d+)", meta).group(1))
     assert scratch == 0, f"rotate+quantize {which}: {scratch} bytes of scratch per lane"
+
+
+def test_mxfp4_scale_loads_between_stages(isa):
+    """The MXFP4 K loop's waits count each 16-byte scale load as issued after a whole stage's
+    transfers; a scale load moved in among a stage's transfers would let a step read a
+    stage before its last transfer landed.  Between two barriers the loop issues one
+    stage's four transfers, then at most one scale load; the prologue issues the first
+    scale load before stage 0 and the second between stages 1 and 2."""
+    body, _ = _function(isa, KERNELS["mxfp4"][0])
+    seq = []
+    for line in body:
+        t = line.strip()
+        if t.startswith("buffer_load_dwordx4") and " lds" in t:
+            seq.append("d")
+        elif t.startswith("buffer_load_dwordx4 v["):
+            seq.append("S")
+        elif t.startswith("s_barrier"):
+            seq.append("|")
+    text = "".join(seq)
+    first = text.index("|")
+    assert text[:first] == "S" + "d" * 8 + "S" + "d" * 4, text[:first]
+    for part in text[first + 1:].split("|"):
+        assert re.fullmatch(r"(d{4}S?)?", part), f"transfers and scale loads between barriers: {part}"
