@@ -48,7 +48,13 @@
  *     recorded by stream capture into a HIP graph and replayed.
  *   - Every call validates its arguments on the host first and returns a status; on error
  *     nothing is enqueued and no output is written.
- *   - Inputs must be finite; NaN or Inf inputs give unspecified codes and scales.
+ *   - Non-finite rows: the rotation runs as an fp32 butterfly whose stage sums reach up to
+ *     2^(k+1) max|x| (k = log4 g), so inputs above FLT_MAX / 2^(k+1) (4.2e37 for g = 16,
+ *     2.1e37, 1.1e37, 5.3e36 for g = 64, 256, 1024; 8.5e37 for rows of equal values) can
+ *     overflow it.  A row whose butterfly overflows, or that holds a NaN or an Inf, gets a
+ *     NaN scale (int4, int8) and unspecified codes, so a layer's output row is NaN; with
+ *     MXFP4 codes, every block of a window holding a non-finite rotated value gets the
+ *     E8M0 NaN byte 0xFF.  No such input yields a finite scale.
  */
 #ifndef CONVROT_H
 #define CONVROT_H

@@ -23,10 +23,13 @@
 //     within the error bound of the row's fp32 max (typically one per row) is recomputed
 //     exactly in fp64 by one wavefront from the raw inputs, and the row max is taken over
 //     those exact values.
-//   * Codes: fma(y, 7/absmax, 1.5*2^23 + 8) rounds y*7/absmax half-to-even and leaves
-//     code + 8 in the low four mantissa bits; eight codes are merged into one dword with
-//     shift-or and byte-permute, then converted from offset binary to two's complement.
+//   * Codes: fma(y, r, 1.5*2^23 + 8), r = the hardware reciprocal of absmax/7, rounds y*r
+//     half-to-even and leaves code + 8 in the low four mantissa bits; eight codes are merged
+//     into one dword with shift-or and byte-permute, then converted from offset binary to
+//     two's complement.
 //   * Packed codes go through LDS so every lane writes 8-32 contiguous bytes.
+//   * The absolute maxima propagate NaN, so a row whose butterfly overflowed fp32 (inputs
+//     above FLT_MAX / 2^(k+1) can do that) or that holds a NaN or an Inf gets a NaN scale.
 #include "rht_quant_device.h"
 
 #include <algorithm>

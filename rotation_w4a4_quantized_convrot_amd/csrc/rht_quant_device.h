@@ -124,12 +124,20 @@ __device__ __forceinline__ void rotate_window(float (&v)[Geo<G>::E]) {
   }
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum over the L lanes of a unit of absolute maxima.  Their bit patterns order as
+// unsigned integers (non-negative floats; a NaN or Inf above every finite value), so the
+// steps are integer maxima, one DPP instruction each.
 template <int L>
-__device__ __forceinline__ float unit_max(float m) {
-  if constexpr (L >= 2) m = fmaxf(m, dpp_f32<kDppXor1>(m));
-  if constexpr (L >= 4) m = fmaxf(m, dpp_f32<kDppXor2>(m));
-  if constexpr (L >= 8) m = fmaxf(m, dpp_f32<kDppXor7>(m));
-  if constexpr (L >= 16) m = fmaxf(m, dpp_f32<kDppXor15>(m));
+__device__ __forceinline__ uint32_t unit_max(uint32_t m) {
+  if constexpr (L >= 2) m = max(m, dpp_u32<kDppXor1>(m));
+  if constexpr (L >= 4) m = max(m, dpp_u32<kDppXor2>(m));
+  if constexpr (L >= 8) m = max(m, dpp_u32<kDppXor7>(m));
+  if constexpr (L >= 16) m = max(m, dpp_u32<kDppXor15>(m));
   return m;
 }
 
@@ -462,15 +470,18 @@ __device__ __forceinline__ void rht_quant_body(const TIn* __restrict__ x, int M,
 
     rotate_window<G>(v);
 
+    // Absolute maxima with IEEE maximum, which propagates NaN: a window whose fp32 butterfly
+    // overflowed, or that holds a non-finite input, gets a non-finite maximum, which flags
+    // its row (int4 / int8) or block (MXFP4) below.
     float cm[C];
     float ml = 0.0f;
 #pragma unroll
     for (int r = 0; r < C; ++r) {
       float c = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c = fmaxf(c, fabsf(v[8 * r + e]));
+      for (int e = 0; e < 8; ++e) c = __builtin_elementwise_maximum(c, fabsf(v[8 * r + e]));
       cm[r] = c;
-      ml = fmaxf(ml, c);
+      ml = __builtin_elementwise_maximum(ml, c);
     }
     uint32_t packed[C][QB / 4];  // the chunk's 8 codes: one dword (4-bit) or two (int8)
     float mrow = 0.0f;
@@ -479,12 +490,13 @@ __device__ __forceinline__ void rht_quant_body(const TIn* __restrict__ x, int M,
       // MXFP4 (OCP Microscaling v1.0): a 32-value block is chunks r, r ^ 1 of this lane and
       // of the lane with position bit 3 flipped (xor 1); its E8M0 byte is
       // floor(log2(absmax)) - 2 + 127, i.e. absmax's exponent field - 2, clamped at 0.  The
-      // conversion divides by the block scale, rounds to nearest even and saturates at 6.
+      // conversion divides by the block scale, rounds to nearest even and saturates at 6.  A
+      // non-finite block maximum stores 0xFF, the E8M0 encoding of NaN.
 #pragma unroll
       for (int r = 0; r < C; r += 2) {
-        float bm = fmaxf(cm[r], cm[r + 1]);
-        bm = fmaxf(bm, dpp_f32<kDppXor1>(bm));
-        const int eb = max(int(__float_as_uint(bm) >> 23) - 2, 0);
+        uint32_t bm = max(__float_as_uint(cm[r]), __float_as_uint(cm[r + 1]));
+        bm = max(bm, dpp_u32<kDppXor1>(bm));
+        const int eb = bm < 0x7F800000u ? max(int(bm >> 23) - 2, 0) : 0xFF;
         const float xs = eb > 0 ? __uint_as_float(uint32_t(eb) << 23) : 0x1p-127f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -513,10 +525,10 @@ __device__ __forceinline__ void rht_quant_body(const TIn* __restrict__ x, int M,
         }
       }
     } else {
-    const float mu = unit_max<L>(ml);
+    const uint32_t mu = unit_max<L>(__float_as_uint(ml));
     uint32_t* rmax = red + (it & 3) * 2 * R;
     rexact = rmax + R;
-    if (active && lu == 0) atomicMax(&rmax[rloc], __float_as_uint(mu));
+    if (active && lu == 0) atomicMax(&rmax[rloc], mu);
     __syncthreads();
 
     // Scale of the previous block: its exact maxima are complete (they precede this barrier).
@@ -529,15 +541,24 @@ __device__ __forceinline__ void rht_quant_body(const TIn* __restrict__ x, int M,
 
     // Codes use the fp32 maximum; they agree with the exact one except at rounding ties.
     mrow = slot_used ? __uint_as_float(rmax[rloc < R ? rloc : 0]) : 0.0f;
-    // A row whose scale max / q_max falls below 2^-126 (a subnormal scale) would see the
-    // reciprocal q_max / max overflow or lose precision: such rows (rare; the wave branches
-    // only when it holds one) divide each value by the row's fp32 scale instead, as the
-    // definition does, clamp to the code range (a subnormal scale can round down far enough
-    // for a quotient to pass q_max + 1/2) and round with the same magic-number add.  A scale
-    // that underflows to zero gives zero codes, as for an all-zero row.
-    const bool tiny = mrow > 0.0f && mrow < kQmax * 0x1p-126f;
+    // A row whose maximum is not finite (its fp32 butterfly overflowed, or it holds a NaN or
+    // Inf input) gets a NaN scale: its exact-maximum word is set to a NaN here, and no
+    // candidate below passes the NaN threshold that such a maximum gives, so nothing else
+    // writes that word before the scale is read from it.
+    if (active && lu == 0 && j == 0 && !(mrow <= 0x1.fffffep127f)) rexact[rloc] = 0x7FC00000u;
+    // Rows whose scale max / q_max falls below 2^-125 (down to subnormal scales, where the
+    // reciprocal q_max / max would overflow or lose precision) are rare; the wave branches
+    // only when it holds one.  They divide each value by the row's fp32 scale instead, as
+    // the definition does, clamp to the code range (a subnormal scale can round down far
+    // enough for a quotient to pass q_max + 1/2) and round with the same magic-number add.
+    // A scale that underflows to zero gives zero codes, as for an all-zero row.
+    const bool tiny = mrow > 0.0f && mrow < kQmax * 0x1p-125f;
     const bool any_tiny = __ballot(tiny) != 0;
-    const float inv = mrow > 0.0f && !tiny ? kQmax / mrow : 0.0f;
+    // Other rows multiply by the hardware reciprocal (1 ulp) of max / q_max, a normal
+    // number here: the codes depend on it only through quotients within a few ulp of a
+    // rounding tie, which the fp32 maximum leaves open anyway.
+    const float inv =
+        mrow > 0.0f && !tiny ? __builtin_amdgcn_rcpf(mrow * (1.0f / kQmax)) : 0.0f;
     float tiny_scale = 0.0f;
     if (any_tiny) {  // uniform; an opaque copy keeps the division inside the branch
       float m = mrow;

@@ -3,8 +3,9 @@
 
 A row whose largest rotated value is below q_max * 2^-126 has a subnormal scale: there the
 reciprocal q_max / max overflows (int4 below ~2.1e-38, int8 below ~3.7e-37) or loses bits,
-so the kernel divides by the row's fp32 scale instead.  Each launch mixes such rows with
-ordinary ones, so that waves holding both kinds are covered.
+so the kernel divides by the row's fp32 scale instead (for every row below q_max * 2^-125, so
+that the reciprocal it takes elsewhere always has a normal argument).  Each launch mixes such
+rows with ordinary ones, so that waves holding both kinds are covered.
 
 Bars:
   * scales (int4, int8): bit-identical to the oracle's fp32(exact absmax / q_max);
