@@ -49,7 +49,8 @@ KERNELS = {
     "rht_quant_mx4": ("rht_quant_kernel<256, unsigned short, 16, 1", RQ_SRC),
     "mxfp4_gemm": ("quant_gemm_kernel<false, 1, false>", GEMM_SRC),
 }
-CALIB_KERNEL = "mfma_i8_loop"
+# calibration.py's int8 MFMA loop with fixed operands (kind 0)
+CALIB_KERNEL = "mfma_loop<0>("
 
 
 def source_sha256(src) -> str:

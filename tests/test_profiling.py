@@ -101,11 +101,14 @@ def test_counter_summary_derivations(tmp_path):
         (2, GEMM, gemm), (3, GEMM, gemm),
         (4, RQ, {"SQ_INSTS_VALU": 2 * M * Kp // 64, "SQ_INSTS_SALU": M * Kp // 64}),
         (5, RQ, {"SQ_INSTS_VALU": 2 * M * Kp // 64, "SQ_INSTS_SALU": M * Kp // 64})])
-    # calibration: three launches; the counters of the largest one are taken
+    # calibration: three launches of the int8 loop with fixed operands, the counters of the
+    # largest one taken, and a larger launch of another kind (scaled FP4), which is not
+    loop = "void (anonymous namespace)::mfma_loop<{}>(int, int*, unsigned long*)"
     _write_multi(tmp_path / "cal", "calib", [
-        (1, "mfma_i8_loop(int, int*, unsigned long*)", {"SQ_INSTS_MFMA": 10, "SQ_VALU_MFMA_BUSY_CYCLES": 999}),
-        (2, "mfma_i8_loop(int, int*, unsigned long*)", {"SQ_INSTS_MFMA": 1000, "SQ_VALU_MFMA_BUSY_CYCLES": 32000}),
-        (3, "mfma_i8_loop(int, int*, unsigned long*)", {"SQ_INSTS_MFMA": 100, "SQ_VALU_MFMA_BUSY_CYCLES": 1})])
+        (1, loop.format(0), {"SQ_INSTS_MFMA": 10, "SQ_VALU_MFMA_BUSY_CYCLES": 999}),
+        (2, loop.format(0), {"SQ_INSTS_MFMA": 1000, "SQ_VALU_MFMA_BUSY_CYCLES": 32000}),
+        (3, loop.format(0), {"SQ_INSTS_MFMA": 100, "SQ_VALU_MFMA_BUSY_CYCLES": 1}),
+        (4, loop.format(1), {"SQ_INSTS_MFMA": 5000, "SQ_VALU_MFMA_BUSY_CYCLES": 7})])
     stats = tmp_path / "bench_kernel_stats.csv"
     with open(stats, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs",
