@@ -21,6 +21,12 @@ library (the oracle and the layer's library are not involved).
 tiled kernel) at K' = 3072 and output shapes of 64 to 256 tiles, one tile per compute unit,
 with codes drawn uniformly from [-7, 7] (the range the quantizer produces): how the time of
 one tile, and the chip's aggregate rate, change with the number of compute units at work.
+
+``--reference-gemms`` times, at the attention-projection shape (4608 x 3072 x 3072), the
+vendor library's GEMMs next to the layer library's W4A4 GEMM: the int8 GEMM behind
+torch._int_mm (int32 output) with operands 16 q (q uniform in [-8, 7], the values the W4A4
+GEMM feeds its matrix instruction), full-range int8 and zeros, and the bf16 GEMM x @ w^T.
+They are a reference for what the chip sustains on this shape, not part of the layer.
 """
 from __future__ import annotations
 
@@ -104,41 +110,82 @@ GEMM_TILE_SHAPES = ((2048, 2048), (3072, 3072), (4608, 3072), (4096, 3584), (435
                     (4096, 4096))
 
 
-def gemm_tiles(kp: int = 3072, launches: int = 200, batches: int = 5, ramp_sec: float = 0.3,
-               seed: int = 0) -> list:
-    """Median per-launch time of convrot_w4a4_gemm at GEMM_TILE_SHAPES (back-to-back launches
-    after a ramp), with the aggregate rate in POP/s."""
+def _median_launch_us(fn, launches: int, batches: int, ramp_sec: float) -> float:
+    """Median over `batches` of the mean time of `launches` back-to-back calls of `fn`, timed
+    with events on the current stream after `ramp_sec` of untimed calls."""
     import time
+    import torch
+    t0 = time.time()
+    while time.time() - t0 < ramp_sec:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    per = []
+    for _ in range(batches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(launches):
+            fn()
+        b.record()
+        b.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / launches)
+    return statistics.median(per)
+
+
+def _packed_codes(rows: int, cols: int, gen, lo: int = -7, hi: int = 7):
+    """Packed int4 codes (two per byte, column 2j in the low nibble), uniform in [lo, hi]."""
+    import torch
+    q = torch.randint(lo, hi + 1, (rows, cols), generator=gen, dtype=torch.int16) & 0xF
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8)
+
+
+def reference_gemms(M: int = 4608, N: int = 3072, K: int = 3072, launches: int = 200,
+                    batches: int = 5, ramp_sec: float = 0.3, seed: int = 0) -> list:
+    """Median per-launch time of the vendor int8 and bf16 GEMMs and of convrot_w4a4_gemm at
+    one shape, with the rate in POP/s (2 M N K per launch)."""
     import torch
     import rotation_w4a4_quantized_convrot_amd as cr
     dev = torch.device("cuda:0")
     gen = torch.Generator(device="cpu").manual_seed(seed)
+    out = []
 
-    def codes(rows):  # two nibbles per byte, each uniform over [-7, 7] (two's complement)
-        q = torch.randint(-7, 8, (rows, kp), generator=gen, dtype=torch.int16) & 0xF
-        return (q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8).to(dev)
+    def add(name, fn):
+        us = _median_launch_us(fn, launches, batches, ramp_sec)
+        out.append({"gemm": name, "M": M, "N": N, "K": K, "us": us,
+                    "pops": 2.0 * M * N * K / (us * 1e-6) / 1e15})
 
+    for data, lo, hi, mul in (("16q", -8, 7, 16), ("int8_full", -128, 127, 1), ("zeros", 0, 0, 1)):
+        a = (torch.randint(lo, hi + 1, (M, K), generator=gen, dtype=torch.int32) * mul).to(torch.int8)
+        w = (torch.randint(lo, hi + 1, (N, K), generator=gen, dtype=torch.int32) * mul).to(torch.int8)
+        a, w = a.to(dev), w.to(dev)
+        add(f"vendor_int8_int32out_{data}", lambda a=a, w=w: torch._int_mm(a, w.t()))
+    x = torch.randn(M, K, generator=gen).to(torch.bfloat16).to(dev)
+    w = torch.randn(N, K, generator=gen).to(torch.bfloat16).to(dev)
+    add("vendor_bf16", lambda: x @ w.t())
+    xq, wq = _packed_codes(M, K, gen).to(dev), _packed_codes(N, K, gen).to(dev)
+    xs = (torch.rand(M, generator=gen) * 1e-2 + 1e-3).to(dev)
+    ws = (torch.rand(N, generator=gen) * 1e-2 + 1e-3).to(dev)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    add("convrot_w4a4_bf16out_codes_-7_7", lambda: cr.convrot_w4a4_gemm(xq, xs, wq, ws, None, y))
+    return out
+
+
+def gemm_tiles(kp: int = 3072, launches: int = 200, batches: int = 5, ramp_sec: float = 0.3,
+               seed: int = 0) -> list:
+    """Median per-launch time of convrot_w4a4_gemm at GEMM_TILE_SHAPES (back-to-back launches
+    after a ramp), with the aggregate rate in POP/s."""
+    import torch
+    import rotation_w4a4_quantized_convrot_amd as cr
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device="cpu").manual_seed(seed)
     out = []
     for M, N in GEMM_TILE_SHAPES:
-        xq, wq = codes(M), codes(N)
+        xq, wq = _packed_codes(M, kp, gen).to(dev), _packed_codes(N, kp, gen).to(dev)
         xs = (torch.rand(M, generator=gen) * 1e-2 + 1e-3).to(dev)
         ws = (torch.rand(N, generator=gen) * 1e-2 + 1e-3).to(dev)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        t0 = time.time()
-        while time.time() - t0 < ramp_sec:
-            for _ in range(20):
-                cr.convrot_w4a4_gemm(xq, xs, wq, ws, None, y)
-            torch.cuda.synchronize()
-        per = []
-        for _ in range(batches):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(launches):
-                cr.convrot_w4a4_gemm(xq, xs, wq, ws, None, y)
-            b.record()
-            b.synchronize()
-            per.append(a.elapsed_time(b) * 1e3 / launches)
-        us = statistics.median(per)
+        us = _median_launch_us(lambda: cr.convrot_w4a4_gemm(xq, xs, wq, ws, None, y),
+                               launches, batches, ramp_sec)
         tiles = -(-M // 256) * -(-N // 256)
         out.append({"M": M, "N": N, "Kp": kp, "tiles": tiles, "us": us,
                     "pops": 2.0 * M * N * kp / (us * 1e-6) / 1e15})
@@ -151,13 +198,24 @@ def main(argv=None) -> int:
     p.add_argument("--command", default=None, help="the command line to record in the summary")
     p.add_argument("--gemm-tiles", action="store_true",
                    help="time the W4A4 GEMM at 64 to 256 tiles instead (layer library)")
+    p.add_argument("--reference-gemms", action="store_true",
+                   help="time the vendor int8 and bf16 GEMMs and the W4A4 GEMM at 4608 x 3072 x 3072")
     a = p.parse_args(argv)
     if a.command is None:
         a.command = "python -m rotation_w4a4_quantized_convrot_amd.calibration" + (
-            " --gemm-tiles" if a.gemm_tiles else "")
+            " --gemm-tiles" if a.gemm_tiles else "") + (
+            " --reference-gemms" if a.reference_gemms else "")
     import torch
     name = torch.cuda.get_device_properties(0).name
-    if a.gemm_tiles:
+    if a.reference_gemms:
+        rows = reference_gemms()
+        lines = ["# GEMMs at 4608 x 3072 x 3072 (attention projection): the vendor library's int8 "
+                 "(torch._int_mm, int32 output) and bf16 (x @ w^T) GEMMs and convrot_w4a4_gemm "
+                 "(int4 codes, bf16 output with the dequantization epilogue); median per-launch "
+                 "time of 5 batches of 200 back-to-back launches; pops = 2 M N K / time",
+                 f"# command (repository root): {a.command}",
+                 f"device={name}; cus={torch.cuda.get_device_properties(0).multi_processor_count}"]
+    elif a.gemm_tiles:
         rows = gemm_tiles()
         lines = ["# W4A4 GEMM (256 x 256 tiles, one per CU) at K' = 3072, codes uniform in "
                  "[-7, 7]: median per-launch time of 5 batches of 200 back-to-back launches",

@@ -36,3 +36,19 @@ def test_gemm_tiles_mode():
     rows = C.gemm_tiles(launches=5, batches=1, ramp_sec=0.01)
     assert [r["tiles"] for r in rows] == [64, 144, 216, 224, 255, 256]
     assert all(r["us"] > 0 and 0 < r["pops"] < C.PEAK_INT8_POPS / 1e15 for r in rows)
+
+
+def test_reference_gemms_mode():
+    """The reference GEMM timing: one row per GEMM, positive times, rates below the published
+    peak of the GEMM's type (int8 5.0 POP/s, bf16 2.5 PFLOP/s)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rotation_w4a4_quantized_convrot_amd import calibration as C
+    print("\n[case] calibration reference_gemms launches=5 batches=1", flush=True)
+    rows = C.reference_gemms(launches=5, batches=1, ramp_sec=0.01)
+    assert [r["gemm"] for r in rows] == [
+        "vendor_int8_int32out_16q", "vendor_int8_int32out_int8_full", "vendor_int8_int32out_zeros",
+        "vendor_bf16", "convrot_w4a4_bf16out_codes_-7_7"]
+    for r in rows:
+        peak = 2.5 if r["gemm"] == "vendor_bf16" else C.PEAK_INT8_POPS / 1e15
+        assert r["us"] > 0 and 0 < r["pops"] < peak, r
