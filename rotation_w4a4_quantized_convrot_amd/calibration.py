@@ -27,6 +27,10 @@ vendor library's GEMMs next to the layer library's W4A4 GEMM: the int8 GEMM behi
 torch._int_mm (int32 output) with operands 16 q (q uniform in [-8, 7], the values the W4A4
 GEMM feeds its matrix instruction), full-range int8 and zeros, and the bf16 GEMM x @ w^T.
 They are a reference for what the chip sustains on this shape, not part of the layer.
+
+``--reference-copies`` times plain device copies (torch's copy kernel): one moving the bytes
+of the attention-projection rotate+quantize (28.3 MB read + 7.1 MB written, here as 17.7 MB
+each way), and larger ones, as the practical ceiling of a streaming kernel of that size.
 """
 from __future__ import annotations
 
@@ -170,6 +174,39 @@ def reference_gemms(M: int = 4608, N: int = 3072, K: int = 3072, launches: int =
     return out
 
 
+# bytes each way: half the attention projection's rotate+quantize traffic (35,407,872 B),
+# 256 MiB and 1 GiB
+COPY_SIZES = (17_703_936, 1 << 28, 1 << 30)
+
+
+def reference_copies(launches: int = 200, batches: int = 5, ramp_sec: float = 0.3) -> list:
+    """Median per-launch time of a device-to-device copy of each size in COPY_SIZES (fewer
+    launches per batch for the large ones), with the rate over the bytes read plus written.
+    Copies smaller than 256 MiB cycle through buffer pairs of at least 600 MB each way, so
+    that, as for the benchmark's rotating inputs, the data comes from HBM and not from the
+    256 MB Infinity Cache."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = []
+    for n in COPY_SIZES:
+        pairs = 1 if n >= (1 << 28) else -(-600_000_000 // n)
+        src = [torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(pairs)]
+        dst = [torch.empty_like(t) for t in src]
+        turn = [0]
+
+        def copy():
+            i = turn[0] % pairs
+            turn[0] += 1
+            dst[i].copy_(src[i])
+
+        k = max(5, launches * COPY_SIZES[0] // n)
+        us = _median_launch_us(copy, k, batches, ramp_sec)
+        out.append({"copy_bytes_each_way": n, "buffer_pairs": pairs, "launches": k, "us": us,
+                    "tb_s": 2.0 * n / (us * 1e-6) / 1e12, "frac_of_8tb_s": 2.0 * n / (us * 1e-6) / 8e12})
+        del src, dst
+    return out
+
+
 def gemm_tiles(kp: int = 3072, launches: int = 200, batches: int = 5, ramp_sec: float = 0.3,
                seed: int = 0) -> list:
     """Median per-launch time of convrot_w4a4_gemm at GEMM_TILE_SHAPES (back-to-back launches
@@ -200,14 +237,23 @@ def main(argv=None) -> int:
                    help="time the W4A4 GEMM at 64 to 256 tiles instead (layer library)")
     p.add_argument("--reference-gemms", action="store_true",
                    help="time the vendor int8 and bf16 GEMMs and the W4A4 GEMM at 4608 x 3072 x 3072")
+    p.add_argument("--reference-copies", action="store_true",
+                   help="time plain device copies of the rotate+quantize bytes and larger")
     a = p.parse_args(argv)
     if a.command is None:
         a.command = "python -m rotation_w4a4_quantized_convrot_amd.calibration" + (
             " --gemm-tiles" if a.gemm_tiles else "") + (
-            " --reference-gemms" if a.reference_gemms else "")
+            " --reference-gemms" if a.reference_gemms else "") + (
+            " --reference-copies" if a.reference_copies else "")
     import torch
     name = torch.cuda.get_device_properties(0).name
-    if a.reference_gemms:
+    if a.reference_copies:
+        rows = reference_copies()
+        lines = ["# device-to-device copies (torch's copy kernel): median per-launch time of 5 "
+                 "batches of back-to-back launches; tb_s = (bytes read + bytes written) / time",
+                 f"# command (repository root): {a.command}",
+                 f"device={name}; cus={torch.cuda.get_device_properties(0).multi_processor_count}"]
+    elif a.reference_gemms:
         rows = reference_gemms()
         lines = ["# GEMMs at 4608 x 3072 x 3072 (attention projection): the vendor library's int8 "
                  "(torch._int_mm, int32 output) and bf16 (x @ w^T) GEMMs and convrot_w4a4_gemm "

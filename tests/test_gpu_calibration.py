@@ -52,3 +52,14 @@ def test_reference_gemms_mode():
     for r in rows:
         peak = 2.5 if r["gemm"] == "vendor_bf16" else C.PEAK_INT8_POPS / 1e15
         assert r["us"] > 0 and 0 < r["pops"] < peak, r
+
+
+def test_reference_copies_mode():
+    """The reference copies: one row per size, rates below the published 8 TB/s."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rotation_w4a4_quantized_convrot_amd import calibration as C
+    print("\n[case] calibration reference_copies launches=5 batches=1", flush=True)
+    rows = C.reference_copies(launches=5, batches=1, ramp_sec=0.01)
+    assert [r["copy_bytes_each_way"] for r in rows] == list(C.COPY_SIZES)
+    assert all(r["us"] > 0 and 0 < r["tb_s"] < 8.0 for r in rows), rows
