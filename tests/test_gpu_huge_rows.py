@@ -136,3 +136,36 @@ def test_huge_rows_layer_output(cr, fmt):
     yf = y.float().cpu().numpy()
     assert np.all(np.isnan(yf[[OVERFLOW, NAN_ROW, INF_ROW]])), fmt
     assert np.all(np.isfinite(yf[[0, 8]])), fmt
+
+
+@pytest.mark.parametrize("entry", ["two_kernel_tiled", "fused", "noalloc"])
+def test_huge_rows_other_paths(cr, entry):
+    """The same flag through the tiled GEMM (600 rows, 4096 outputs), the single-launch layer
+    and the entry point without a workspace: flagged rows' outputs are NaN, the others finite
+    and bit-identical to the two-kernel layer's."""
+    g, K = 256, 1000
+    M, N = (600, 4096) if entry == "two_kernel_tiled" else (64, 256)
+    print(f"\n[case] huge rows {entry} M={M} K={K} N={N}", flush=True)
+    _, xt, _ = _rows(g, K, "bf16", seed=11)
+    x = torch.from_numpy(np.random.default_rng(12).standard_normal((M, K))).to(torch.bfloat16)
+    x[:9] = xt
+    x = x.to(DEV)
+    w = torch.from_numpy(np.random.default_rng(13).standard_normal((N, K))).to(torch.bfloat16).to(DEV)
+    bias = torch.zeros(N, dtype=torch.bfloat16, device=DEV)
+    wq, ws = cr.convrot_quant_weight(w, g)
+    ref = cr.convrot_w4a4_linear(x, g, wq, ws, bias)
+    if entry == "fused":
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        y = cr.convrot_w4a4_linear_fused(x, g, wq, ws, bias, status=status)
+    elif entry == "noalloc":
+        y = cr.convrot_w4a4_linear_noalloc(x, g, wq, ws, bias)
+    else:
+        y = ref
+    torch.cuda.synchronize()
+    if entry == "fused":
+        assert status.item() == 0
+    yf = y.float().cpu().numpy()
+    assert np.all(np.isnan(yf[[OVERFLOW, NAN_ROW, INF_ROW]])), entry
+    rest = np.r_[0, 8, 9:M]
+    assert np.all(np.isfinite(yf[rest])), entry
+    assert torch.equal(y[rest].view(torch.int16), ref[rest].view(torch.int16)), entry
