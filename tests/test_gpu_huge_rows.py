@@ -169,3 +169,23 @@ def test_huge_rows_other_paths(cr, entry):
     rest = np.r_[0, 8, 9:M]
     assert np.all(np.isfinite(yf[rest])), entry
     assert torch.equal(y[rest].view(torch.int16), ref[rest].view(torch.int16)), entry
+
+
+@pytest.mark.parametrize("g", [16, 256, 1024])
+def test_huge_weight_rows(cr, g):
+    """Weight rows go through the same kernel: huge rows in range match the oracle's weight
+    quantization, flagged rows get NaN scales, and the layer's output columns for them are
+    NaN while the others stay finite."""
+    K = 3 * g + g // 2
+    print(f"\n[case] huge weight rows g={g} K={K}", flush=True)
+    wh, wt, _ = _rows(g, K, "bf16", seed=300 + g)
+    wq, ws = cr.convrot_quant_weight(wt.to(DEV), g)
+    torch.cuda.synchronize()
+    check_rotate_quant(wq[GOOD], ws[GOOD], None, O.quantize_weight(wh[GOOD], g), f"weights g={g}")
+    _flagged_scales(ws)
+    x = torch.from_numpy(np.random.default_rng(301).standard_normal((5, K))).to(torch.bfloat16).to(DEV)
+    y = cr.convrot_w4a4_linear(x, g, wq, ws, None)
+    torch.cuda.synchronize()
+    yf = y.float().cpu().numpy()
+    assert np.all(np.isnan(yf[:, [OVERFLOW, NAN_ROW, INF_ROW]]))
+    assert np.all(np.isfinite(yf[:, [0, 8]]))
