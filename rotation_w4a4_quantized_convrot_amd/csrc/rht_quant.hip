@@ -110,6 +110,12 @@ hipError_t launch_plan(const TIn* x, int64_t M, int64_t K, int64_t ldx, int64_t 
     p.waves = (W + U - 1) / U;
   }
   if (p.waves > MW) return hipErrorInvalidValue;
+  // Fewer blocks than compute units: one row per block, so that the few rows spread over
+  // as many workgroups as there are rows (64 x 3072, g = 256: 4.70 against 4.92 us).
+  if (p.R > 1 && (M + p.R - 1) / p.R < device_cus()) {
+    p.R = 1;
+    p.waves = (W + U - 1) / U;
+  }
   const int nblocks = int((M + p.R - 1) / p.R);
   const size_t shmem = rq_shmem(p.R, p.waves, U, G, int(sizeof(TIn)), fmt_bits<FMT>(),
                                 FMT != kFmtMx4);
